@@ -1,0 +1,275 @@
+"""Benchmark of the ternary-weight FP16 GEMM on one MI355X.
+
+One step = one pass of the hot path over the K = 8192 workloads:
+  * TQ2, M in {1, 2, 4, 8, 16, 32, 64, 128} on (K, N) = (8192, 8192) and (8192, 28672)
+    (i.i.d. trits with P(0) = 0.31, fp16 block scales ~ U(0.01, 0.03));
+  * TQ1, M in {1, 4, 16, 64} on the same two shapes (P(0) = 0.3).
+Weights, scales and activations are resident in HBM before timing starts; every
+call reads its own copy from a ring of buffer sets (>= 1 GiB per shape and
+format) so that nothing is served from the 256 MB Infinity Cache.
+
+Printed: one JSON line.  ``value`` is the step's fraction of the roofline,
+sum over calls of max(bytes / 8 TB/s, flops / 2.5 PFLOP/s) divided by the
+measured step time.  Per-call TB/s, TFLOP/s and fractions are in ``calls``.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_F16_PEAK = 2.5e15     # dense FP16 MFMA flop/s
+K_MAIN = 8192
+SHAPES = [(8192, 8192), (8192, 28672)]  # (K, N)
+TQ2_MS = [1, 2, 4, 8, 16, 32, 64, 128]
+TQ1_MS = [1, 4, 16, 64]
+RING_BYTES = 1 << 30
+
+
+def tq1_ldq(K):
+    return (-(-K // 5) + 15) // 16 * 16
+
+
+def alg_bytes(fmt, M, N, K):
+    """Bytes the method must move: packed weights, scales, X, Y."""
+    w = N * K // 4 if fmt == "tq2" else N * tq1_ldq(K)
+    return w + 2 * N * (K // 256) + 2 * M * K + 2 * M * N
+
+
+def alg_flops(M, N, K):
+    return 2 * M * N * K
+
+
+def t_roof(fmt, M, N, K):
+    return max(alg_bytes(fmt, M, N, K) / HBM_PEAK, alg_flops(M, N, K) / MFMA_F16_PEAK)
+
+
+def workload_calls():
+    calls = []
+    for K, N in SHAPES:
+        for M in TQ2_MS:
+            calls.append(("tq2", M, N, K))
+    for K, N in SHAPES:
+        for M in TQ1_MS:
+            calls.append(("tq1", M, N, K))
+    return calls
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- GPU
+
+def build_inputs(torch, tq, calls):
+    from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
+    rings = {}
+    for fmt, M, N, K in calls:
+        key = (fmt, N, K)
+        if key in rings:
+            continue
+        rng = seed_for(500, N, K, 1 if fmt == "tq2" else 2)
+        T = ternary_iid(rng, N, K, 0.31 if fmt == "tq2" else 0.3)
+        s = block_scales_fp16(rng, N, K)
+        qs = tq.tq_pack_tq2(T)[0] if fmt == "tq2" else tq.tq_pack_tq1(T)[0]
+        del T
+        per_set = qs.nbytes + s.nbytes
+        R = max(2, -(-RING_BYTES // per_set))
+        q0 = torch.from_numpy(qs).cuda()
+        s0 = torch.from_numpy(s).cuda()
+        ring = [(q0, s0)] + [(q0.clone(), s0.clone()) for _ in range(R - 1)]
+        rings[key] = {"sets": ring, "next": 0}
+        log(f"[bench] {fmt} N={N} K={K}: {R} buffer sets of {per_set / 1e6:.1f} MB")
+    xs = {}
+    for fmt, M, N, K in calls:
+        if (M, K) not in xs:
+            xs[(M, K)] = torch.from_numpy(activations_fp16(seed_for(501, M, K), M, K)).cuda()
+    ys = {(M, N): torch.empty((M, N), dtype=torch.float16, device="cuda") for _, M, N, _ in calls}
+    return rings, xs, ys
+
+
+def run_call(tq, fmt, M, N, K, rings, xs, ys, stream):
+    r = rings[(fmt, N, K)]
+    q, s = r["sets"][r["next"]]
+    r["next"] = (r["next"] + 1) % len(r["sets"])
+    X, Y = xs[(M, K)], ys[(M, N)]
+    if fmt == "tq2":
+        st = tq.lib.tq_gemm_tq2(X.data_ptr(), q.data_ptr(), s.data_ptr(), Y.data_ptr(), M, N, K,
+                                stream)
+    else:
+        st = tq.lib.tq_gemm_tq1(X.data_ptr(), q.data_ptr(), q.shape[1], s.data_ptr(),
+                                Y.data_ptr(), M, N, K, stream)
+    if st != 0:
+        raise RuntimeError(f"tq_gemm_{fmt} failed: {tq.tq_status_string(st)}")
+
+
+def gpu_bench(args):
+    import torch
+    import bit_mixed_precision_amd.binding as tq
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    torch.cuda.set_device(0)
+    calls = workload_calls()
+    rings, xs, ys = build_inputs(torch, tq, calls)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for c in calls:
+            run_call(tq, *c, rings, xs, ys, sptr)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup done ({args.warmup} steps)")
+
+    # Timed region: K steps; one event pair around each call, recorded on the
+    # stream the kernels run on.
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in calls] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for k in range(args.steps):
+        for i, c in enumerate(calls):
+            ev[k][i][0].record(stream)
+            run_call(tq, *c, rings, xs, ys, sptr)
+            ev[k][i][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t0.elapsed_time(t1) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)")
+
+    per_call = []
+    for i, (fmt, M, N, K) in enumerate(calls):
+        us = float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)])) * 1e3
+        b, f = alg_bytes(fmt, M, N, K), alg_flops(M, N, K)
+        tr = t_roof(fmt, M, N, K)
+        per_call.append({
+            "fmt": fmt, "M": M, "N": N, "K": K,
+            "kernel": tq.tq_kernel_name(2 if fmt == "tq2" else 1, M, N, K),
+            "us": round(us, 3), "TBps": round(b / us / 1e6, 3), "TFLOPps": round(f / us / 1e6, 2),
+            "bound": "hbm" if b / HBM_PEAK >= f / MFMA_F16_PEAK else "mfma",
+            "hbm_frac": round(b / HBM_PEAK / (us * 1e-6), 4),
+            "mfma_frac": round(f / MFMA_F16_PEAK / (us * 1e-6), 4),
+            "roof_frac": round(tr / (us * 1e-6), 4),
+        })
+    return calls, per_call, ms_step
+
+
+def roofline_of(per_call):
+    """Roofline object for the kernel that takes the most time in the step."""
+    by_kernel = {}
+    for c in per_call:
+        by_kernel.setdefault(c["kernel"], []).append(c)
+    dom = max(by_kernel, key=lambda k: sum(c["us"] for c in by_kernel[k]))
+    cs = by_kernel[dom]
+    t = sum(c["us"] for c in cs) * 1e-6
+    nbytes = sum(alg_bytes(c["fmt"], c["M"], c["N"], c["K"]) for c in cs)
+    flops = sum(alg_flops(c["M"], c["N"], c["K"]) for c in cs)
+    hbm_bound = nbytes / HBM_PEAK >= flops / MFMA_F16_PEAK
+    if hbm_bound:
+        achieved, peak, unit = nbytes / t / 1e9, HBM_PEAK / 1e9, "GB/s"
+    else:
+        achieved, peak, unit = flops / t / 1e12, MFMA_F16_PEAK / 1e12, "TFLOP/s"
+    return {"kernel": dom, "bound": "hbm" if hbm_bound else "mfma",
+            "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "launches_per_step": len(cs),
+            "avg_launch_us": round(t / len(cs) * 1e6, 3)}
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(calls, cols=1024):
+    """The fp64 oracle on the host: each call of the step on ``cols`` sampled
+    output columns, time scaled by N / cols."""
+    from oracle import gemm_ref
+    from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    weights = {}
+    total_t = total_roof = total_bytes = total_flops = 0.0
+    for fmt, M, N, K in calls:
+        key = (fmt, K)
+        if key not in weights:
+            rng = seed_for(600, K, 1 if fmt == "tq2" else 2)
+            weights[key] = (ternary_iid(rng, cols, K, 0.31), block_scales_fp16(rng, cols, K))
+        T, s = weights[key]
+        X = activations_fp16(seed_for(601, M, K), M, K)
+        t = time.perf_counter()
+        gemm_ref(X, T, s)
+        dt = (time.perf_counter() - t) * (N / cols)
+        total_t += dt
+        total_roof += t_roof(fmt, M, N, K)
+        total_bytes += alg_bytes(fmt, M, N, K)
+        total_flops += alg_flops(M, N, K)
+    return {"value": round(total_roof / total_t, 8), "unit": "fraction of MI355X roofline",
+            "cores": threads, "kind": "oracle",
+            "sample": f"every call of one step on {cols} sampled output columns (fp64 dequantize + "
+                      f"numpy matmul), time scaled by N/{cols}",
+            "s_per_step": round(total_t, 3),
+            "TBps": round(total_bytes / total_t / 1e12, 6),
+            "TFLOPps": round(total_flops / total_t / 1e12, 6)}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calls-out", default=None, help="also write the per-call table here (JSON)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the product has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    calls, per_call, ms_step = gpu_bench(args)
+    roof_sum = sum(t_roof(*c) for c in calls)
+    value = roof_sum / (ms_step * 1e-3)
+    out = {
+        "metric": "ternary GEMM TB/s + TFLOP/s vs roofline at M=1..128, K=8192 (TQ2, TQ1)",
+        "value": round(value, 4),
+        "unit": "fraction of roofline (HBM 8 TB/s, FP16 MFMA 2.5 PFLOP/s)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16", "data": "synthetic",
+        "config": {"workload": "TQ2 batch sweep M=1..128 and TQ1 M in {1,4,16,64} on "
+                               "(K,N)=(8192,8192),(8192,28672); i.i.d. trits, fp16 block scales",
+                   "global_batch": None, "seq_len": None, "parallelism": "none"},
+        "roofline": roofline_of(per_call),
+    }
+    hbm = [c for c in per_call if c["bound"] == "hbm"]
+    mf = [c for c in per_call if c["bound"] == "mfma"]
+    out["hbm_bound_calls"] = {"n": len(hbm), "mean_hbm_frac": round(float(np.mean([c["hbm_frac"] for c in hbm])), 4) if hbm else None}
+    out["mfma_bound_calls"] = {"n": len(mf), "mean_mfma_frac": round(float(np.mean([c["mfma_frac"] for c in mf])), 4) if mf else None}
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle) ...")
+        out["cpu_baseline"] = cpu_baseline(calls)
+    out["calls"] = per_call
+    if args.calls_out:
+        with open(args.calls_out, "w") as f:
+            json.dump(per_call, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+"""Python binding of libtq.so: the C entry points under the same names.
+
+Argument marshalling only.  Host functions take numpy arrays; device functions
+take torch tensors that already live on the GPU and pass their data pointers
+and the current HIP stream.  Every status other than TQ_OK raises ``TQError``.
+Importing this module raises ``ImportError`` when libtq.so has not been built:
+there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing; build it with "
+                      "`python -m bit_mixed_precision_amd.build_lib`")
+lib = C.CDLL(_LIB_PATH)
+
+TQ_OK, TQ_ERR_NULL, TQ_ERR_SHAPE, TQ_ERR_VALUE, TQ_ERR_ALIGN, TQ_ERR_DEVICE, TQ_ERR_UNSUPPORTED = \
+    0, -1, -2, -3, -4, -5, -6
+TQ_SRC_TERNARY_I8, TQ_SRC_LATENT_F32 = 0, 1
+TQ_PATH_AUTO, TQ_PATH_SKINNY, TQ_PATH_TILED, TQ_PATH_SIMPLE = 0, 1, 2, 3
+
+_P, _I64, _I, _D = C.c_void_p, C.c_int64, C.c_int, C.c_double
+
+#: Every symbol include/tq.h declares, with (restype, argtypes).
+SIGNATURES = {
+    "tq_status_string": (C.c_char_p, [_I]),
+    "tq_abi_version": (_I, []),
+    "tq_tq2_bytes": (_I64, [_I64, _I64]),
+    "tq_tq1_ldq": (_I64, [_I64]),
+    "tq_num_scales": (_I64, [_I64, _I64]),
+    "tq_ternarize_f32": (_I, [_P, _I64, _I64, _D, _P, _P]),
+    "tq_pack_tq2": (_I, [_I, _P, _I64, _I64, _D, _P, _P, _P]),
+    "tq_pack_tq1": (_I, [_I, _P, _I64, _I64, _D, _I64, _P, _P, _P]),
+    "tq_unpack_tq2": (_I, [_P, _I64, _I64, _P]),
+    "tq_unpack_tq1": (_I, [_P, _I64, _I64, _I64, _P]),
+    "tq_gemm_tq2": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "tq_gemm_tq1": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _P]),
+    "tq_kernel_name": (_I, [_I, _I64, _I64, _I64, _I, C.c_char_p, _I64]),
+    "tq_gemm_tq2_ex": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
+    "tq_gemm_tq1_ex": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _P]),
+}
+for _name, (_res, _args) in SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {tq_status_string(status)} ({status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != TQ_OK:
+        raise TQError(status, where)
+
+
+def _ptr(a) -> int | None:
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    return a.data_ptr()  # torch tensor
+
+
+def tq_status_string(status: int) -> str:
+    return lib.tq_status_string(status).decode()
+
+
+def tq_abi_version() -> int:
+    return lib.tq_abi_version()
+
+
+def tq_tq2_bytes(N: int, K: int) -> int:
+    return lib.tq_tq2_bytes(N, K)
+
+
+def tq_tq1_ldq(K: int) -> int:
+    return lib.tq_tq1_ldq(K)
+
+
+def tq_num_scales(N: int, K: int) -> int:
+    return lib.tq_num_scales(N, K)
+
+
+# ------------------------------------------------------------------ host
+
+def tq_ternarize_f32(W: np.ndarray, eps: float = 1e-5):
+    """(T int8 [N][K], gamma) for float32 latents W [N][K]."""
+    W = np.ascontiguousarray(W, dtype=np.float32)
+    N, K = W.shape
+    T = np.empty((N, K), dtype=np.int8)
+    g = C.c_double(0.0)
+    _check(lib.tq_ternarize_f32(_ptr(W), N, K, float(eps), _ptr(T), C.byref(g)), "tq_ternarize_f32")
+    return T, g.value
+
+
+def _src(W):
+    W = np.asarray(W)
+    if W.dtype == np.int8:
+        return TQ_SRC_TERNARY_I8, np.ascontiguousarray(W)
+    if W.dtype == np.float32:
+        return TQ_SRC_LATENT_F32, np.ascontiguousarray(W)
+    raise TypeError("W must be int8 trits or float32 latents")
+
+
+def tq_pack_tq2(W: np.ndarray, eps: float = 1e-5):
+    """Pack int8 trits or float32 latents W [N][K].
+
+    Returns (qs uint8 [N][K/4], scales fp16 [N][K/256] or None, gamma or None);
+    scales and gamma come back only for latents (fp16(gamma) in every block).
+    """
+    kind, W = _src(W)
+    N, K = W.shape
+    qs = np.empty((N, max(K // 4, 0)), dtype=np.uint8)
+    scales = np.empty((N, max(K // 256, 0)), dtype=np.float16) if kind == TQ_SRC_LATENT_F32 else None
+    g = C.c_double(0.0)
+    _check(lib.tq_pack_tq2(kind, _ptr(W), N, K, float(eps), _ptr(qs), _ptr(scales), C.byref(g)),
+           "tq_pack_tq2")
+    return qs, scales, (g.value if scales is not None else None)
+
+
+def tq_pack_tq1(W: np.ndarray, eps: float = 1e-5, ldq: int | None = None):
+    """Like tq_pack_tq2 with the 1.6-bit packing; qs is uint8 [N][ldq]."""
+    kind, W = _src(W)
+    N, K = W.shape
+    if ldq is None:
+        ldq = tq_tq1_ldq(K)
+    qs = np.empty((N, max(ldq, 0)), dtype=np.uint8)
+    scales = np.empty((N, max(K // 256, 0)), dtype=np.float16) if kind == TQ_SRC_LATENT_F32 else None
+    g = C.c_double(0.0)
+    _check(lib.tq_pack_tq1(kind, _ptr(W), N, K, float(eps), ldq, _ptr(qs), _ptr(scales),
+                           C.byref(g)), "tq_pack_tq1")
+    return qs, scales, (g.value if scales is not None else None)
+
+
+def tq_unpack_tq2(qs: np.ndarray, K: int) -> np.ndarray:
+    qs = np.ascontiguousarray(qs, dtype=np.uint8)
+    N = qs.shape[0]
+    if qs.shape[1] * 4 != K:
+        raise ValueError("qs does not hold K/4 bytes per row")
+    T = np.empty((N, K), dtype=np.int8)
+    _check(lib.tq_unpack_tq2(_ptr(qs), N, K, _ptr(T)), "tq_unpack_tq2")
+    return T
+
+
+def tq_unpack_tq1(qs: np.ndarray, K: int) -> np.ndarray:
+    qs = np.ascontiguousarray(qs, dtype=np.uint8)
+    N, ldq = qs.shape
+    T = np.empty((N, K), dtype=np.int8)
+    _check(lib.tq_unpack_tq1(_ptr(qs), N, K, ldq, _ptr(T)), "tq_unpack_tq1")
+    return T
+
+
+# ------------------------------------------------------------------ device
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _out(Y, M, N, like):
+    if Y is not None:
+        return Y
+    import torch
+    return torch.empty((M, N), dtype=torch.float16, device=like.device)
+
+
+def tq_gemm_tq2_ex(X, qs, scales, path: int, Y=None, stream=None):
+    """Y[M][N] = X[M][K] (s . T)^T for TQ2 weights qs [N][K/4]; tensors on the GPU."""
+    M, K = X.shape
+    N = qs.shape[0]
+    Y = _out(Y, M, N, X)
+    _check(lib.tq_gemm_tq2_ex(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, path,
+                              _stream(stream)), "tq_gemm_tq2")
+    return Y
+
+
+def tq_gemm_tq1_ex(X, qs, scales, path: int, Y=None, stream=None):
+    """Same as tq_gemm_tq2_ex for TQ1 weights qs [N][ldq] (ldq = qs.shape[1])."""
+    M, K = X.shape
+    N, ldq = qs.shape
+    Y = _out(Y, M, N, X)
+    _check(lib.tq_gemm_tq1_ex(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K, path,
+                              _stream(stream)), "tq_gemm_tq1")
+    return Y
+
+
+def tq_gemm_tq2(X, qs, scales, Y=None, stream=None):
+    return tq_gemm_tq2_ex(X, qs, scales, TQ_PATH_AUTO, Y, stream)
+
+
+def tq_gemm_tq1(X, qs, scales, Y=None, stream=None):
+    return tq_gemm_tq1_ex(X, qs, scales, TQ_PATH_AUTO, Y, stream)
+
+
+def tq_kernel_name(fmt: int, M: int, N: int, K: int, path: int = TQ_PATH_AUTO) -> str:
+    """Kernel that the product with this format (2 or 1), shape and path runs."""
+    buf = C.create_string_buffer(128)
+    _check(lib.tq_kernel_name(fmt, M, N, K, path, buf, 128), "tq_kernel_name")
+    return buf.value.decode()
+
+
+def raw_call(name: str, *args) -> int:
+    """Call a C entry point with raw arguments and return its status (for tests)."""
+    return getattr(lib, name)(*args)

@@ -1,0 +1,129 @@
+// C ABI of the device GEMMs (include/tq.h): argument checks and kernel choice.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+#include "tq_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxMN = int64_t(1) << 24;
+constexpr int64_t kMaxK = int64_t(1) << 20;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Null -> shape -> alignment, in that order.  Returns TQ_OK or an error code;
+// *noop is set when M or N is zero (nothing to do, no pointer is touched).
+int check_gemm(const void* X, const void* qs, const void* scales, const void* Y, int64_t M,
+               int64_t N, int64_t K, bool tq1, int64_t ldq, bool* noop) {
+  *noop = false;
+  if (M < 0 || N < 0) return TQ_ERR_SHAPE;
+  if (M == 0 || N == 0) {
+    *noop = true;
+    return TQ_OK;
+  }
+  if (!X || !qs || !scales || !Y) return TQ_ERR_NULL;
+  if (M > kMaxMN || N > kMaxMN || K < 256 || K % 256 || K > kMaxK) return TQ_ERR_SHAPE;
+  if (tq1 && (ldq < (K + 4) / 5 || ldq % 16)) return TQ_ERR_SHAPE;
+  if (!aligned16(X) || !aligned16(qs) || !aligned16(scales) || !aligned16(Y)) return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
+
+int device_ready() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return TQ_ERR_DEVICE;
+  }
+  return TQ_OK;
+}
+
+int finish(hipError_t e) {
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return TQ_ERR_DEVICE;
+  }
+  return TQ_OK;
+}
+
+using Launcher = hipError_t (*)(const tq::GemmArgs&, hipStream_t);
+
+struct Choice {
+  Launcher launch;   // nullptr when the path is not available
+  const char* name;  // kernel symbol family, as profilers list it
+};
+
+// The kernel each (format, M, path) runs.  Shapes are already validated.
+Choice choose(bool tq1, int64_t M, int path) {
+  (void)M;
+  switch (path) {
+    case TQ_PATH_AUTO:
+    case TQ_PATH_SIMPLE:
+      return tq1 ? Choice{tq::launch_tq1_simple, "tq1_simple_kernel"}
+                 : Choice{tq::launch_tq2_simple, "tq2_simple_kernel"};
+    default:
+      return Choice{nullptr, ""};
+  }
+}
+
+int run(bool tq1, const tq::GemmArgs& a, int path, hipStream_t s) {
+  Choice c = choose(tq1, a.M, path);
+  if (!c.launch) return TQ_ERR_UNSUPPORTED;
+  return finish(c.launch(a, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int tq_gemm_tq2_ex(const void* X, const void* qs, const void* scales, void* Y, int64_t M,
+                   int64_t N, int64_t K, int path, void* stream) {
+  bool noop = false;
+  int st = check_gemm(X, qs, scales, Y, M, N, K, false, 0, &noop);
+  if (st != TQ_OK || noop) return st;
+  if (path < TQ_PATH_AUTO || path > TQ_PATH_SIMPLE) return TQ_ERR_VALUE;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  tq::GemmArgs a{X, qs, scales, Y, M, N, K, 0};
+  return run(false, a, path, static_cast<hipStream_t>(stream));
+}
+
+int tq_gemm_tq1_ex(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,
+                   int64_t M, int64_t N, int64_t K, int path, void* stream) {
+  bool noop = false;
+  int st = check_gemm(X, qs, scales, Y, M, N, K, true, ldq, &noop);
+  if (st != TQ_OK || noop) return st;
+  if (path < TQ_PATH_AUTO || path > TQ_PATH_SIMPLE) return TQ_ERR_VALUE;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  tq::GemmArgs a{X, qs, scales, Y, M, N, K, ldq};
+  return run(true, a, path, static_cast<hipStream_t>(stream));
+}
+
+int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* name,
+                   int64_t cap) {
+  if (!name) return TQ_ERR_NULL;
+  if (M < 1 || N < 1 || M > kMaxMN || N > kMaxMN || K < 256 || K % 256 || K > kMaxK || cap < 1)
+    return TQ_ERR_SHAPE;
+  if ((format != 1 && format != 2) || path < TQ_PATH_AUTO || path > TQ_PATH_SIMPLE)
+    return TQ_ERR_VALUE;
+  Choice c = choose(format == 1, M, path);
+  if (!c.launch) return TQ_ERR_UNSUPPORTED;
+  int64_t i = 0;
+  for (; c.name[i] && i + 1 < cap; ++i) name[i] = c.name[i];
+  name[i] = '\0';
+  return TQ_OK;
+}
+
+int tq_gemm_tq2(const void* X, const void* qs, const void* scales, void* Y, int64_t M, int64_t N,
+                int64_t K, void* stream) {
+  return tq_gemm_tq2_ex(X, qs, scales, Y, M, N, K, TQ_PATH_AUTO, stream);
+}
+
+int tq_gemm_tq1(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,
+                int64_t M, int64_t N, int64_t K, void* stream) {
+  return tq_gemm_tq1_ex(X, qs, ldq, scales, Y, M, N, K, TQ_PATH_AUTO, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,23 @@
+// Internal launchers of the GEMM kernels.  Callers (tq_api.hip) have already
+// validated every argument: shapes, alignment and sizes are as include/tq.h
+// states, and M, N >= 1.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+struct GemmArgs {
+  const void* X;       // fp16 [M][K]
+  const void* qs;      // TQ2: uint8 [N][K/4]; TQ1: uint8 [N][ldq]
+  const void* scales;  // fp16 [N][K/256]
+  void* Y;             // fp16 [M][N]
+  int64_t M, N, K;
+  int64_t ldq;  // TQ1 row stride in bytes (unused for TQ2)
+};
+
+hipError_t launch_tq2_simple(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_tq1_simple(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace tq

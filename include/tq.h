@@ -1,0 +1,158 @@
+/*
+ * tq.h -- C ABI of the ternary-weight FP16 GEMM library (libtq.so), gfx950.
+ *
+ * The library computes Y = X (gamma T)^T, with FP16 activations X and ternary
+ * weights T in {-1, 0, 1} stored in one of two lossless packings, as defined on
+ * the project page "Scaling Laws and Efficient Inference for Ternary Language
+ * Models":
+ *   - "The model", steps 1-3: gamma = eps + mean|W| over the whole matrix,
+ *     T = round(clip(W / gamma, -1, 1)), Y = X (gamma T)^T;
+ *   - "Packing ternary weights" / "2 bits per weight" (TQ2): d' = d + 1 in a
+ *     2-bit field, d' = (b >> 2j) & 3, four weights per byte;
+ *   - "Packing ternary weights" / "1.6 bits per weight" (TQ1): five shifted
+ *     digits read as a base-3 number N in [0, 242], stored as
+ *     b = floor((256 N + 242) / 243);
+ *   - "Fast inference on CPUs": one 16-bit scale per block of 256 weights;
+ *   - "TriRun: ternary inference on GPUs": FP32 accumulation, FP16 output.
+ *
+ * Layouts (all row-major, no padding unless stated):
+ *   X       fp16 [M][K]
+ *   Y       fp16 [M][N]            Y[m][n] = sum_k X[m][k] * s[n][k/256] * T[n][k]
+ *   T       int8 [N][K]            row n is output feature n (as nn.Linear)
+ *   scales  fp16 [N][K/256]        s[n][b] scales weights k in [256 b, 256 b + 256)
+ *   TQ2 qs  uint8 [N][K/4]         weight k = 4 i + j of a row: byte i, bits 2j..2j+1
+ *   TQ1 qs  uint8 [N][ldq]         byte g of a row: weights 5 g .. 5 g + 4, the first
+ *                                  one most significant; the last group of a row is
+ *                                  padded with zero trits; bytes ceil(K/5) .. ldq-1
+ *                                  are written as 0 and never read for values.
+ *
+ * Every function returns an int status (TQ_OK = 0, errors < 0).  No function
+ * throws, aborts or prints.  Arguments are checked in this order: null
+ * pointers, shapes, alignment, values; argument errors are reported before any
+ * output is written or any kernel launched.  The caller owns every buffer.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_NULL = -1,        /* a required pointer is NULL                         */
+  TQ_ERR_SHAPE = -2,       /* negative or unsupported M, N, K, ldq               */
+  TQ_ERR_VALUE = -3,       /* trit outside {-1,0,1}, NaN/Inf latent, gamma <= 0,  */
+                           /* invalid packed byte                                 */
+  TQ_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned            */
+  TQ_ERR_DEVICE = -5,      /* no usable HIP device, or a launch failed           */
+  TQ_ERR_UNSUPPORTED = -6  /* an option this build does not provide              */
+};
+
+/* Source of the weights handed to the packers. */
+typedef enum {
+  TQ_SRC_TERNARY_I8 = 0, /* int8 [N][K] trits in {-1, 0, 1}                        */
+  TQ_SRC_LATENT_F32 = 1  /* float [N][K] latent weights, ternarized with eps        */
+} tq_src;
+
+/* Kernel family for tq_gemm_*_ex.  AUTO picks the skinny kernel for M <= 16 and
+ * the tiled MFMA kernel above; the others force one family at any M (used by
+ * the tests to cover both sides of the switch). */
+typedef enum {
+  TQ_PATH_AUTO = 0,
+  TQ_PATH_SKINNY = 1,
+  TQ_PATH_TILED = 2,
+  TQ_PATH_SIMPLE = 3 /* one wave per output row, VALU only: the plain GPU kernel */
+} tq_path;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* tq_status_string(int status);
+
+/* Version of this ABI; bumped on any incompatible change. */
+int tq_abi_version(void);
+
+/* Buffer sizes, in elements (bytes for qs).  Return -1 for invalid shapes. */
+int64_t tq_tq2_bytes(int64_t N, int64_t K);  /* N * K / 4                           */
+int64_t tq_tq1_ldq(int64_t K);               /* ceil(K / 5) rounded up to 16         */
+int64_t tq_num_scales(int64_t N, int64_t K); /* N * K / 256                          */
+
+/* ---------------------------------------------------------------------------
+ * Host side (offline).  Thread-safe and stateless; uses several host threads
+ * for large matrices.  All pointers are host memory.
+ * ------------------------------------------------------------------------- */
+
+/* "The model", steps 1-2.  W float [N][K], N, K >= 1.  gamma = eps + S / (N K),
+ * where S is the exactly rounded fp64 sum of |W|; each trit is the fp64
+ * quotient W / gamma clipped to [-1, 1] and rounded half to even.
+ * T (int8 [N][K]) may be NULL to obtain gamma only; gamma_out may be NULL.
+ * Errors: TQ_ERR_VALUE for a NaN/Inf weight, or a gamma that is not finite and
+ * positive (e.g. eps = 0 and W = 0). */
+int tq_ternarize_f32(const float* W, int64_t N, int64_t K, double eps,
+                     int8_t* T, double* gamma_out);
+
+/* TQ2 packing ("2 bits per weight").  K must be a positive multiple of 256.
+ *   kind = TQ_SRC_LATENT_F32: W is float [N][K]; ternarize as tq_ternarize_f32,
+ *     write qs, fill every entry of scales (fp16 bits [N][K/256]) with fp16(gamma)
+ *     rounded to nearest even in one step from fp64, and store gamma in
+ *     *gamma_out when non-NULL.  scales must not be NULL.
+ *   kind = TQ_SRC_TERNARY_I8: W is int8 [N][K]; only qs is written; scales,
+ *     gamma_out and eps are ignored (scales may be NULL).
+ * qs is uint8 [N][K/4]. */
+int tq_pack_tq2(int kind, const void* W, int64_t N, int64_t K, double eps,
+                uint8_t* qs, uint16_t* scales_f16, double* gamma_out);
+
+/* TQ1 packing ("1.6 bits per weight").  Same kinds and scales as tq_pack_tq2;
+ * qs is uint8 [N][ldq] with ldq >= ceil(K/5).  K must be a positive multiple
+ * of 256 (the scale block); the rows' last group is padded with zero trits. */
+int tq_pack_tq1(int kind, const void* W, int64_t N, int64_t K, double eps, int64_t ldq,
+                uint8_t* qs, uint16_t* scales_f16, double* gamma_out);
+
+/* Inverse of the packers: T int8 [N][K].  K >= 1 (a multiple of 4 for TQ2).
+ * TQ_ERR_VALUE for a 2-bit field equal to 3 (TQ2), for one of the 13 byte values
+ * that no pattern produces, or for a non-zero padding trit (TQ1). */
+int tq_unpack_tq2(const uint8_t* qs, int64_t N, int64_t K, int8_t* T);
+int tq_unpack_tq1(const uint8_t* qs, int64_t N, int64_t K, int64_t ldq, int8_t* T);
+
+/* ---------------------------------------------------------------------------
+ * Device side.  Every pointer is device memory on the current HIP device.
+ * The call only enqueues work on `stream` (a hipStream_t; NULL = the default
+ * stream) and returns; it allocates nothing, never synchronizes and uses no
+ * atomics, so Y is the same bit for bit on every run with the same inputs.
+ *
+ *   Y = X (s . T)^T :  X fp16 [M][K], Y fp16 [M][N], scales fp16 [N][K/256].
+ *
+ * Shapes: M, N >= 0 (M == 0 or N == 0 is a no-op that touches no pointer);
+ * K a positive multiple of 256; M, N <= 2^24, K <= 2^20.  For TQ1, ldq >=
+ * ceil(K/5) and ldq % 16 == 0.  X, qs, scales and Y must be 16-byte aligned.
+ * Accumulation is fp32; Y is rounded to fp16 (nearest even) once, overflow
+ * gives +-inf.  Trits are not validated on the device: a TQ2 field equal to 3
+ * or an unused TQ1 byte gives unspecified (finite) values for that row.
+ * Errors: TQ_ERR_DEVICE when no HIP device is usable or the launch fails.
+ * ------------------------------------------------------------------------- */
+int tq_gemm_tq2(const void* X, const void* qs, const void* scales_f16, void* Y,
+                int64_t M, int64_t N, int64_t K, void* stream);
+int tq_gemm_tq1(const void* X, const void* qs, int64_t ldq, const void* scales_f16, void* Y,
+                int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Name of the kernel that tq_gemm_tq2_ex (format = 2) or tq_gemm_tq1_ex
+ * (format = 1) launches for this shape and path, as profilers show it, copied
+ * NUL-terminated into name[cap].  TQ_ERR_SHAPE for an invalid shape,
+ * TQ_ERR_VALUE for an unknown format or path, TQ_ERR_NULL for a NULL name,
+ * TQ_ERR_UNSUPPORTED when the path is not available for the format.  Host
+ * only; touches no device. */
+int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* name,
+                   int64_t cap);
+
+/* Same as above with an explicit kernel family (tq_path). */
+int tq_gemm_tq2_ex(const void* X, const void* qs, const void* scales_f16, void* Y,
+                   int64_t M, int64_t N, int64_t K, int path, void* stream);
+int tq_gemm_tq1_ex(const void* X, const void* qs, int64_t ldq, const void* scales_f16, void* Y,
+                   int64_t M, int64_t N, int64_t K, int path, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H_ */

@@ -1,0 +1,46 @@
+"""Helpers shared by the GPU parity tests (not collected by pytest)."""
+
+import functools
+
+import numpy as np
+
+from oracle import gemm_ref
+from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
+
+#: Acceptance bound of the product: max|Y - Y_ref| <= REL_TOL * max|Y_ref|.
+REL_TOL = 4e-3
+
+
+def check_close(Y, Yref, label=""):
+    """Y (fp16, any array-like) against the fp64 oracle; returns the error in
+    units of max|Y_ref| and of fp16 ulps of |Y_ref| for logging."""
+    Y64 = np.asarray(Y, dtype=np.float64)
+    Yref = np.asarray(Yref, dtype=np.float64)
+    assert Y64.shape == Yref.shape, (label, Y64.shape, Yref.shape)
+    assert np.all(np.isfinite(Y64)), label
+    big = float(np.max(np.abs(Yref))) if Yref.size else 0.0
+    err = float(np.max(np.abs(Y64 - Yref))) if Yref.size else 0.0
+    if big == 0.0:
+        assert err == 0.0, (label, err)
+        return 0.0, 0.0
+    ulp = np.spacing(np.abs(Yref).astype(np.float16)).astype(np.float64)
+    ulp_err = float(np.max(np.abs(Y64 - Yref) / np.maximum(ulp, 2.0 ** -24)))
+    assert err <= REL_TOL * big, f"{label}: max err {err:.3e} > {REL_TOL} * {big:.3e} (ulps {ulp_err:.1f})"
+    return err / big, ulp_err
+
+
+@functools.lru_cache(maxsize=8)
+def iid_problem(N, K, p_zero, seed):
+    """Ternary weights i.i.d. and U(0.01, 0.03) block scales (numpy, host)."""
+    rng = seed_for(seed, N, K, int(p_zero * 1000))
+    T = ternary_iid(rng, N, K, p_zero)
+    s = block_scales_fp16(rng, N, K)
+    return T, s
+
+
+def activations(M, K, seed):
+    return activations_fp16(seed_for(seed, M, K, 99), M, K)
+
+
+def ref(X, T, s, cols=None):
+    return gemm_ref(X, T, s, cols=cols)

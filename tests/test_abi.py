@@ -1,0 +1,112 @@
+"""libtq.so loads, exports every symbol include/tq.h declares, and rejects bad
+arguments with the documented codes before touching memory (CPU only)."""
+
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+tq = pytest.importorskip("bit_mixed_precision_amd.binding")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+HAS_GPU = os.path.exists("/dev/kfd")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = _declared()
+    assert len(names) >= 14
+    out = subprocess.run(["nm", "-D", "--defined-only", tq._LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (tq_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    assert set(names) == set(tq.SIGNATURES)
+    for n in names:
+        assert hasattr(tq.lib, n)
+
+
+def test_status_and_sizes():
+    assert tq.tq_abi_version() == 1
+    assert tq.tq_status_string(0) == "ok"
+    assert tq.tq_status_string(-4).startswith("pointer")
+    assert tq.tq_status_string(123) == "unknown status"
+    assert tq.tq_tq2_bytes(8192, 8192) == 16777216
+    assert tq.tq_tq2_bytes(8192, 28672) * 1 == 58720256
+    assert tq.tq_num_scales(8192, 8192) * 2 == 524288
+    assert tq.tq_tq1_ldq(8192) == 1648 and tq.tq_tq1_ldq(1024) == 208
+    assert tq.tq_tq2_bytes(-1, 4) == -1 and tq.tq_num_scales(1, 100) == -1
+
+
+A = 0x10000  # a 16-byte aligned fake address: never dereferenced by the checks below
+
+
+def _g2(X=A, q=A, s=A, Y=A, M=1, N=16, K=256, path=0):
+    return tq.raw_call("tq_gemm_tq2_ex", X, q, s, Y, M, N, K, path, None)
+
+
+def _g1(X=A, q=A, ldq=64, s=A, Y=A, M=1, N=16, K=256, path=0):
+    return tq.raw_call("tq_gemm_tq1_ex", X, q, ldq, s, Y, M, N, K, path, None)
+
+
+def test_gemm_argument_errors():
+    # null -> shape -> alignment -> value, each before any device work
+    assert _g2(X=None) == tq.TQ_ERR_NULL
+    assert _g2(Y=None, K=100) == tq.TQ_ERR_NULL
+    assert _g2(K=100) == tq.TQ_ERR_SHAPE
+    assert _g2(K=0) == tq.TQ_ERR_SHAPE
+    assert _g2(M=-1) == tq.TQ_ERR_SHAPE
+    assert _g2(M=(1 << 24) + 1) == tq.TQ_ERR_SHAPE
+    assert _g2(K=(1 << 20) + 256) == tq.TQ_ERR_SHAPE
+    assert _g2(X=A + 8, K=100) == tq.TQ_ERR_SHAPE
+    assert _g2(X=A + 8) == tq.TQ_ERR_ALIGN
+    assert _g2(s=A + 2) == tq.TQ_ERR_ALIGN
+    assert _g2(path=9) == tq.TQ_ERR_VALUE
+    assert _g1(ldq=51) == tq.TQ_ERR_SHAPE      # < ceil(256/5)
+    assert _g1(ldq=56) == tq.TQ_ERR_SHAPE      # not a multiple of 16
+    assert _g1(q=A + 4) == tq.TQ_ERR_ALIGN
+    # empty products are no-ops that touch no pointer
+    assert _g2(X=None, q=None, s=None, Y=None, M=0) == tq.TQ_OK
+    assert _g1(X=None, q=None, s=None, Y=None, N=0) == tq.TQ_OK
+    assert tq.raw_call("tq_gemm_tq2", None, None, None, None, 0, 5, 256, None) == tq.TQ_OK
+
+
+@pytest.mark.skipif(HAS_GPU, reason="checks the no-device error; a GPU is present")
+def test_gemm_without_device():
+    assert _g2() == tq.TQ_ERR_DEVICE
+    assert _g1() == tq.TQ_ERR_DEVICE
+    assert tq.raw_call("tq_gemm_tq2", A, A, A, A, 4, 32, 512, None) == tq.TQ_ERR_DEVICE
+
+
+def test_host_argument_errors():
+    P = C.c_void_p
+    buf = (C.c_uint8 * 4096)()
+    assert tq.raw_call("tq_pack_tq2", 0, None, 1, 256, 0.0, buf, None, None) == tq.TQ_ERR_NULL
+    assert tq.raw_call("tq_pack_tq2", 1, buf, 1, 256, 0.0, buf, None, None) == tq.TQ_ERR_NULL
+    assert tq.raw_call("tq_pack_tq2", 5, buf, 1, 256, 0.0, buf, buf, None) == tq.TQ_ERR_VALUE
+    assert tq.raw_call("tq_pack_tq2", 0, buf, 0, 256, 0.0, buf, None, None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_pack_tq1", 0, buf, 1, 256, 0.0, 10, buf, None, None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_unpack_tq2", None, 1, 4, buf) == tq.TQ_ERR_NULL
+    assert tq.raw_call("tq_unpack_tq2", buf, 1, 6, buf) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_unpack_tq1", buf, 1, 5, 0, buf) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_ternarize_f32", None, 1, 1, 0.0, None, None) == tq.TQ_ERR_NULL
+    assert tq.raw_call("tq_ternarize_f32", P(C.addressof(buf)), 0, 1, 0.0, None, None) == tq.TQ_ERR_SHAPE
+
+
+def test_package_fails_loudly_without_library(tmp_path):
+    """A copy of the package without libtq.so raises ImportError on use."""
+    import shutil
+    pkg = tmp_path / "bit_mixed_precision_amd"
+    shutil.copytree(os.path.join(ROOT, "bit_mixed_precision_amd"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    code = ("import bit_mixed_precision_amd as b\n"
+            "try:\n    b.tq_gemm_tq2\nexcept ImportError as e:\n    print('IMPORT-ERROR', e)\n")
+    out = subprocess.run(["python", "-c", code], cwd=tmp_path, capture_output=True, text=True)
+    assert "IMPORT-ERROR" in out.stdout, out.stdout + out.stderr

@@ -1,0 +1,233 @@
+"""GPU parity: tq_gemm_tq2 / tq_gemm_tq1 through the C ABI against the fp64 oracle.
+
+Bar: max|Y - Y_ref| <= 4e-3 * max|Y_ref| (Y is the fp16 GPU output widened to
+fp64); exact equality where the product is exactly representable (identity,
+permutations, one weight per row, zero weights).  Every kernel family is forced
+at every M through the *_ex entry points, so both sides of the M switch are
+covered.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from gpu_util import activations, check_close, iid_problem, ref
+from oracle import pack_tq1_ref, pack_tq2_ref, ternarize_ref
+from synth import latent_weights_f32, seed_for
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+tq = pytest.importorskip("bit_mixed_precision_amd.binding")
+
+PATHS = {"simple": 3, "skinny": 1, "tiled": 2, "auto": 0}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.cuda()
+
+
+def run(fmt, X, qs, s, path, Y=None):
+    Xd, qd, sd = (x if torch.is_tensor(x) else dev(x) for x in (X, qs, s))
+    if fmt == "tq2":
+        Yd = tq.tq_gemm_tq2_ex(Xd, qd, sd, PATHS[path], Y)
+    else:
+        Yd = tq.tq_gemm_tq1_ex(Xd, qd, sd, PATHS[path], Y)
+    torch.cuda.synchronize()
+    return Yd
+
+
+def pack(fmt, T):
+    if fmt == "tq2":
+        return tq.tq_pack_tq2(T)[0]
+    return tq.tq_pack_tq1(T)[0]
+
+
+def supported(fmt, path):
+    X = torch.zeros((1, 256), dtype=torch.float16, device="cuda")
+    s = torch.ones((16, 1), dtype=torch.float16, device="cuda")
+    q = torch.zeros((16, 64 if fmt == "tq2" else 64), dtype=torch.uint8, device="cuda")
+    Y = torch.empty((1, 16), dtype=torch.float16, device="cuda")
+    fn = tq.lib.tq_gemm_tq2_ex if fmt == "tq2" else None
+    if fmt == "tq2":
+        st = fn(X.data_ptr(), q.data_ptr(), s.data_ptr(), Y.data_ptr(), 1, 16, 256, PATHS[path],
+                None)
+    else:
+        st = tq.lib.tq_gemm_tq1_ex(X.data_ptr(), q.data_ptr(), 64, s.data_ptr(), Y.data_ptr(), 1,
+                                   16, 256, PATHS[path], None)
+    torch.cuda.synchronize()
+    return st != tq.TQ_ERR_UNSUPPORTED
+
+
+def need(fmt, path):
+    if not supported(fmt, path):
+        pytest.skip(f"{path} kernel family not available for {fmt}")
+
+
+SMALL = [(1, 1024, 1024), (2, 48, 512), (3, 100, 768), (4, 17, 256), (8, 130, 1280),
+         (9, 64, 512), (16, 257, 2048), (17, 96, 768), (32, 40, 1024), (33, 200, 512),
+         (64, 128, 1536), (100, 77, 256), (128, 300, 1024)]
+
+
+@pytest.mark.parametrize("path", ["simple", "skinny", "tiled", "auto"])
+@pytest.mark.parametrize("fmt", ["tq2", "tq1"])
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_parity(fmt, path, M, N, K):
+    need(fmt, path)
+    say(f"[small] {fmt} {path} M={M} N={N} K={K}")
+    T, s = iid_problem(N, K, 0.31, 1)
+    X = activations(M, K, 1)
+    Y = run(fmt, X, pack(fmt, T), s, path).cpu().numpy()
+    check_close(Y, ref(X, T, s), f"{fmt}/{path}/{M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("path", ["simple", "skinny", "tiled"])
+@pytest.mark.parametrize("fmt", ["tq2", "tq1"])
+def test_exact_special_cases(fmt, path):
+    """Identity, minus identity, permutation, zero, one weight per row: exact."""
+    need(fmt, path)
+    K = 512
+    for M in (1, 5, 16, 40):
+        say(f"[exact] {fmt} {path} M={M}")
+        X = activations(M, K, 2)
+        one = np.ones((K, K // 256), np.float16)
+        I = np.eye(K, dtype=np.int8)
+        Y = run(fmt, X, pack(fmt, I), one, path).cpu().numpy()
+        assert np.array_equal(Y.view(np.uint16), X.view(np.uint16))
+        Y = run(fmt, X, pack(fmt, -I), one, path).cpu().numpy()
+        assert np.array_equal(Y, -X)
+        perm = seed_for(3).permutation(K)
+        Y = run(fmt, X, pack(fmt, I[perm]), one, path).cpu().numpy()
+        assert np.array_equal(Y.view(np.uint16), X[:, perm].view(np.uint16))
+        Z = np.zeros((48, K), np.int8)
+        Y = run(fmt, X, pack(fmt, Z), np.ones((48, 2), np.float16), path).cpu().numpy()
+        assert not np.any(Y.view(np.uint16))  # +0 everywhere
+        # one nonzero per row with block scales: Y = fp16(+-x * s), exact product
+        N = 64
+        cols = seed_for(4).integers(0, K, N)
+        sign = np.where(seed_for(5).random(N) < 0.5, -1, 1).astype(np.int8)
+        T = np.zeros((N, K), np.int8)
+        T[np.arange(N), cols] = sign
+        s = iid_problem(N, K, 0.31, 6)[1]
+        Y = run(fmt, X, pack(fmt, T), s, path).cpu().numpy()
+        want = ref(X, T, s).astype(np.float16)  # exact product, one rounding
+        assert np.array_equal(Y.view(np.uint16), want.view(np.uint16))
+
+
+@pytest.mark.parametrize("path", ["simple", "skinny", "tiled"])
+def test_tq1_ragged_tail(path):
+    """K = 256, 768, 1280: 5 does not divide K, the last group carries padding."""
+    need("tq1", path)
+    for K in (256, 768, 1280, 3072):
+        T, s = iid_problem(40, K, 0.5, 7)
+        T = T.copy()
+        T[:, -1] = 1  # the last real weight of each row is non-zero
+        X = activations(3, K, 7)
+        Y = run("tq1", X, pack("tq1", T), s, path).cpu().numpy()
+        check_close(Y, ref(X, T, s), f"tq1 tail K={K}")
+
+
+def test_cross_format_same_weights():
+    """TQ2 and TQ1 packings of the same (T, s) give the same Y_ref, and both GPU
+    results meet the bar."""
+    N, K = 512, 2048
+    for p in (0.3, 0.5, 0.9):
+        T, s = iid_problem(N, K, p, 8)
+        for M in (1, 4, 16, 64):
+            X = activations(M, K, 8)
+            R = ref(X, T, s)
+            Y2 = run("tq2", X, pack("tq2", T), s, "auto").cpu().numpy()
+            Y1 = run("tq1", X, pack("tq1", T), s, "auto").cpu().numpy()
+            check_close(Y2, R, f"tq2 p={p} M={M}")
+            check_close(Y1, R, f"tq1 p={p} M={M}")
+
+
+def test_deterministic_bits():
+    T, s = iid_problem(1024, 4096, 0.31, 9)
+    q2, q1 = dev(pack("tq2", T)), dev(pack("tq1", T))
+    sd = dev(s)
+    for M in (1, 8, 16, 64):
+        X = dev(activations(M, 4096, 9))
+        a = run("tq2", X, q2, sd, "auto").clone()
+        b = run("tq2", X, q2, sd, "auto")
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+        a = run("tq1", X, q1, sd, "auto").clone()
+        b = run("tq1", X, q1, sd, "auto")
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_latent_end_to_end():
+    """Latents -> host packer -> GPU, against the oracle's own ternarization.
+    Shapes: the 1024 x 1024 layer and the 3B-class decode linears at M = 1."""
+    shapes = [(1024, 1024), (3072, 3072), (3072, 8192), (8192, 3072)]
+    for i, (K, N) in enumerate(shapes):
+        say(f"[latent] K={K} N={N}")
+        W = latent_weights_f32(seed_for(20, i), N, K, 0.02)
+        Tr, g = ternarize_ref(W, 1e-5)
+        X = activations(1, K, 20 + i)
+        s_ref = np.full((N, K // 256), np.float16(g))
+        R = ref(X, Tr, s_ref)
+        q2, s2, _ = tq.tq_pack_tq2(W, eps=1e-5)
+        assert np.array_equal(q2, pack_tq2_ref(Tr))
+        check_close(run("tq2", X, q2, s2, "auto").cpu().numpy(), R, f"latent tq2 {K}x{N}")
+        q1, s1, _ = tq.tq_pack_tq1(W, eps=1e-5)
+        assert np.array_equal(q1, pack_tq1_ref(Tr))
+        check_close(run("tq1", X, q1, s1, "auto").cpu().numpy(), R, f"latent tq1 {K}x{N}")
+
+
+FULL_M = [1, 2, 4, 8, 16, 32, 64, 128]
+
+
+@pytest.mark.parametrize("N", [8192, 28672])
+def test_full_size_tq2_sweep(N):
+    """The K = 8192 batch sweep at full size; 256 sampled columns against the oracle,
+    all columns checked for finiteness."""
+    K = 8192
+    T, s = iid_problem(N, K, 0.31, 30)
+    qd, sd = dev(pack("tq2", T)), dev(s)
+    cols = np.sort(seed_for(31, N).choice(N, 256, replace=False))
+    cols[0], cols[-1] = 0, N - 1
+    for M in FULL_M:
+        say(f"[full tq2] N={N} M={M}")
+        X = activations(M, K, 30 + M)
+        Y = run("tq2", X, qd, sd, "auto").cpu().numpy()
+        assert np.all(np.isfinite(Y.astype(np.float32)))
+        check_close(Y[:, cols], ref(X, T, s, cols=cols), f"full tq2 N={N} M={M}")
+
+
+@pytest.mark.parametrize("N", [8192, 28672])
+@pytest.mark.parametrize("p", [0.3, 0.9])
+def test_full_size_tq1(N, p):
+    K = 8192
+    T, s = iid_problem(N, K, p, 40)
+    qd, sd = dev(pack("tq1", T)), dev(s)
+    cols = np.sort(seed_for(41, N).choice(N, 256, replace=False))
+    cols[0], cols[-1] = 0, N - 1
+    for M in (1, 4, 16, 64):
+        say(f"[full tq1] N={N} p={p} M={M}")
+        X = activations(M, K, 40 + M)
+        Y = run("tq1", X, qd, sd, "auto").cpu().numpy()
+        assert np.all(np.isfinite(Y.astype(np.float32)))
+        check_close(Y[:, cols], ref(X, T, s, cols=cols), f"full tq1 N={N} p={p} M={M}")
+
+
+def test_empty_is_noop():
+    X = torch.empty((0, 256), dtype=torch.float16, device="cuda")
+    q = torch.empty((16, 64), dtype=torch.uint8, device="cuda")
+    s = torch.ones((16, 1), dtype=torch.float16, device="cuda")
+    Y = tq.tq_gemm_tq2(X, q, s)
+    assert Y.shape == (0, 16)
