@@ -2,6 +2,9 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdio.h>
+
+#include <atomic>
 
 #include "tq.h"
 #include "tq_kernels.h"
@@ -51,29 +54,59 @@ using Launcher = hipError_t (*)(const tq::GemmArgs&, hipStream_t);
 
 struct Choice {
   Launcher launch;   // nullptr when the path is not available
-  const char* name;  // kernel symbol family, as profilers list it
+  const char* name;  // kernel template, as profilers list it
+  int variant;       // template argument, or -1 for none
 };
 
-// The kernel each (format, M, path) runs.  Shapes are already validated.
-Choice choose(bool tq1, int64_t M, int path) {
-  (void)M;
+constexpr int64_t kSkinnyMaxM = 16;
+
+// The kernel each (format, shape, path) runs.  Shapes are already validated.
+Choice choose(bool tq1, int64_t M, int64_t N, int path) {
+  if (path == TQ_PATH_AUTO) path = (M <= kSkinnyMaxM && !tq1) ? TQ_PATH_SKINNY : TQ_PATH_SIMPLE;
   switch (path) {
-    case TQ_PATH_AUTO:
     case TQ_PATH_SIMPLE:
-      return tq1 ? Choice{tq::launch_tq1_simple, "tq1_simple_kernel"}
-                 : Choice{tq::launch_tq2_simple, "tq2_simple_kernel"};
+      return tq1 ? Choice{tq::launch_tq1_simple, "tq1_simple_kernel", -1}
+                 : Choice{tq::launch_tq2_simple, "tq2_simple_kernel", -1};
+    case TQ_PATH_SKINNY:
+      if (M > kSkinnyMaxM || tq1) return Choice{nullptr, "", -1};
+      return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_rows(N)};
     default:
-      return Choice{nullptr, ""};
+      return Choice{nullptr, "", -1};
   }
 }
 
 int run(bool tq1, const tq::GemmArgs& a, int path, hipStream_t s) {
-  Choice c = choose(tq1, a.M, path);
+  Choice c = choose(tq1, a.M, a.N, path);
   if (!c.launch) return TQ_ERR_UNSUPPORTED;
   return finish(c.launch(a, s));
 }
 
 }  // namespace
+
+namespace tq {
+
+// Compute units of the current device, cached per device; 256 (MI355X) when no
+// device can be queried, so that host-only callers see the MI355X choice.
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0) {
+    (void)hipGetLastError();
+    cus = 256;
+  }
+  cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+}  // namespace tq
 
 extern "C" {
 
@@ -108,10 +141,15 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
     return TQ_ERR_SHAPE;
   if ((format != 1 && format != 2) || path < TQ_PATH_AUTO || path > TQ_PATH_SIMPLE)
     return TQ_ERR_VALUE;
-  Choice c = choose(format == 1, M, path);
+  Choice c = choose(format == 1, M, N, path);
   if (!c.launch) return TQ_ERR_UNSUPPORTED;
+  char buf[160];
+  if (c.variant >= 0)
+    snprintf(buf, sizeof buf, "%s<%d>", c.name, c.variant);
+  else
+    snprintf(buf, sizeof buf, "%s", c.name);
   int64_t i = 0;
-  for (; c.name[i] && i + 1 < cap; ++i) name[i] = c.name[i];
+  for (; buf[i] && i + 1 < cap; ++i) name[i] = buf[i];
   name[i] = '\0';
   return TQ_OK;
 }

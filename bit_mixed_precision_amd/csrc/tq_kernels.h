@@ -17,7 +17,15 @@ struct GemmArgs {
   int64_t ldq;  // TQ1 row stride in bytes (unused for TQ2)
 };
 
+// Number of compute units of the current device (cached per device).
+int device_cus();
+
 hipError_t launch_tq2_simple(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_tq1_simple(const GemmArgs& a, hipStream_t stream);
+
+// Skinny MFMA kernels for M <= 16; skinny_rows(N) is the number of 16-row
+// groups one workgroup owns (the template argument of the kernel).
+int skinny_rows(int64_t N);
+hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace tq
