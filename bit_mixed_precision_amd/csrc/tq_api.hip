@@ -55,23 +55,32 @@ using Launcher = hipError_t (*)(const tq::GemmArgs&, hipStream_t);
 struct Choice {
   Launcher launch;   // nullptr when the path is not available
   const char* name;  // kernel template, as profilers list it
-  int variant;       // template argument, or -1 for none
+  int variant;       // first template argument, or -1 for none
+  int variant2;      // second template argument, or -1 for none
 };
 
 constexpr int64_t kSkinnyMaxM = 16;
 
 // The kernel each (format, shape, path) runs.  Shapes are already validated.
 Choice choose(bool tq1, int64_t M, int64_t N, int path) {
-  if (path == TQ_PATH_AUTO) path = (M <= kSkinnyMaxM && !tq1) ? TQ_PATH_SKINNY : TQ_PATH_SIMPLE;
+  if (path == TQ_PATH_AUTO) {
+    if (tq1) path = TQ_PATH_SIMPLE;
+    else path = M <= kSkinnyMaxM ? TQ_PATH_SKINNY : TQ_PATH_TILED;
+  }
   switch (path) {
     case TQ_PATH_SIMPLE:
-      return tq1 ? Choice{tq::launch_tq1_simple, "tq1_simple_kernel", -1}
-                 : Choice{tq::launch_tq2_simple, "tq2_simple_kernel", -1};
+      return tq1 ? Choice{tq::launch_tq1_simple, "tq1_simple_kernel", -1, -1}
+                 : Choice{tq::launch_tq2_simple, "tq2_simple_kernel", -1, -1};
     case TQ_PATH_SKINNY:
-      if (M > kSkinnyMaxM || tq1) return Choice{nullptr, "", -1};
-      return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_rows(N)};
+      if (M > kSkinnyMaxM || tq1) return Choice{nullptr, "", -1, -1};
+      return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_rows(N), -1};
+    case TQ_PATH_TILED: {
+      if (tq1) return Choice{nullptr, "", -1, -1};
+      const tq::TiledShape t = tq::tiled_shape(M, N);
+      return Choice{tq::launch_tq2_tiled, "tq2_tiled_kernel", t.mt, t.nr};
+    }
     default:
-      return Choice{nullptr, "", -1};
+      return Choice{nullptr, "", -1, -1};
   }
 }
 
@@ -144,7 +153,9 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
   Choice c = choose(format == 1, M, N, path);
   if (!c.launch) return TQ_ERR_UNSUPPORTED;
   char buf[160];
-  if (c.variant >= 0)
+  if (c.variant2 >= 0)
+    snprintf(buf, sizeof buf, "%s<%d, %d>", c.name, c.variant, c.variant2);
+  else if (c.variant >= 0)
     snprintf(buf, sizeof buf, "%s<%d>", c.name, c.variant);
   else
     snprintf(buf, sizeof buf, "%s", c.name);

@@ -28,4 +28,12 @@ hipError_t launch_tq1_simple(const GemmArgs& a, hipStream_t stream);
 int skinny_rows(int64_t N);
 hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream);
 
+// Tiled MFMA kernels for M > 16: a workgroup owns 16 mt activation rows x
+// 16 nr weight rows.
+struct TiledShape {
+  int mt, nr;
+};
+TiledShape tiled_shape(int64_t M, int64_t N);
+hipError_t launch_tq2_tiled(const GemmArgs& a, hipStream_t stream);
+
 }  // namespace tq
