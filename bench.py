@@ -113,6 +113,10 @@ def run_call(tq, fmt, M, N, K, rings, xs, ys, stream):
 
 
 def gpu_bench(args):
+    """Time the step through HIP graphs (one captured graph per timed step, the
+    calls inside rotate through the buffer rings), so host launch overhead is
+    not in the measurement.  Per-call averages come from one graph per call
+    holding `reps` back-to-back launches of that call."""
     import torch
     import bit_mixed_precision_amd.binding as tq
 
@@ -120,39 +124,63 @@ def gpu_bench(args):
     torch.cuda.set_device(0)
     calls = workload_calls()
     rings, xs, ys = build_inputs(torch, tq, calls)
-    stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
     torch.cuda.synchronize()
 
-    for _ in range(args.warmup):
+    # one eager pass: kernel attributes are set outside any capture
+    for c in calls:
+        run_call(tq, *c, rings, xs, ys, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+
+    cap = torch.cuda.Stream()
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                fn(cap.cuda_stream)
+        return g
+
+    def one_step(sp):
         for c in calls:
-            run_call(tq, *c, rings, xs, ys, sptr)
+            run_call(tq, *c, rings, xs, ys, sp)
+
+    n_graphs = args.warmup + args.steps
+    graphs = [capture(one_step) for _ in range(n_graphs)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    for g in graphs[:args.warmup]:
+        g.replay()
     torch.cuda.synchronize()
     log(f"[bench] warmup done ({args.warmup} steps)")
 
-    # Timed region: K steps; one event pair around each call, recorded on the
-    # stream the kernels run on.
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in calls] for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t0.record(stream)
-    for k in range(args.steps):
-        for i, c in enumerate(calls):
-            ev[k][i][0].record(stream)
-            run_call(tq, *c, rings, xs, ys, sptr)
-            ev[k][i][1].record(stream)
+    for g in graphs[args.warmup:]:
+        g.replay()
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t0.elapsed_time(t1) / args.steps
     log(f"[bench] timed {args.steps} steps: {ms_step:.4f} ms/step (wall {wall:.3f} s)")
+    del graphs
 
     per_call = []
-    for i, (fmt, M, N, K) in enumerate(calls):
-        us = float(np.mean([ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(args.steps)])) * 1e3
+    for fmt, M, N, K in calls:
+        reps = args.reps
+        g = capture(lambda sp: [run_call(tq, fmt, M, N, K, rings, xs, ys, sp) for _ in range(reps)])
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        del g
         b, f = alg_bytes(fmt, M, N, K), alg_flops(M, N, K)
         tr = t_roof(fmt, M, N, K)
         per_call.append({
@@ -233,6 +261,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--reps", type=int, default=30, help="launches per call when timing each call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calls-out", default=None, help="also write the per-call table here (JSON)")
     args = ap.parse_args()

@@ -62,9 +62,9 @@ struct Choice {
 constexpr int64_t kSkinnyMaxM = 16;
 
 // The kernel each (format, shape, path) runs.  Shapes are already validated.
-Choice choose(bool tq1, int64_t M, int64_t N, int path) {
+Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
   if (path == TQ_PATH_AUTO) {
-    if (tq1) path = TQ_PATH_SIMPLE;
+    if (tq1) path = TQ_PATH_SKINNY;
     else path = M <= kSkinnyMaxM ? TQ_PATH_SKINNY : TQ_PATH_TILED;
   }
   switch (path) {
@@ -72,8 +72,12 @@ Choice choose(bool tq1, int64_t M, int64_t N, int path) {
       return tq1 ? Choice{tq::launch_tq1_simple, "tq1_simple_kernel", -1, -1}
                  : Choice{tq::launch_tq2_simple, "tq2_simple_kernel", -1, -1};
     case TQ_PATH_SKINNY:
-      if (M > kSkinnyMaxM || tq1) return Choice{nullptr, "", -1, -1};
-      return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_rows(N), -1};
+      if (tq1)
+        return Choice{tq::launch_tq1_skinny, "tq1_skinny_kernel", tq::tq1_depth(),
+                      tq::tq1_stage(N, K)};
+      if (M > kSkinnyMaxM) return Choice{nullptr, "", -1, -1};
+      return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_depth(),
+                    tq::skinny_stage(N, K)};
     case TQ_PATH_TILED: {
       if (tq1) return Choice{nullptr, "", -1, -1};
       const tq::TiledShape t = tq::tiled_shape(M, N);
@@ -85,7 +89,7 @@ Choice choose(bool tq1, int64_t M, int64_t N, int path) {
 }
 
 int run(bool tq1, const tq::GemmArgs& a, int path, hipStream_t s) {
-  Choice c = choose(tq1, a.M, a.N, path);
+  Choice c = choose(tq1, a.M, a.N, a.K, path);
   if (!c.launch) return TQ_ERR_UNSUPPORTED;
   return finish(c.launch(a, s));
 }
@@ -150,10 +154,12 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
     return TQ_ERR_SHAPE;
   if ((format != 1 && format != 2) || path < TQ_PATH_AUTO || path > TQ_PATH_SIMPLE)
     return TQ_ERR_VALUE;
-  Choice c = choose(format == 1, M, N, path);
+  Choice c = choose(format == 1, M, N, K, path);
   if (!c.launch) return TQ_ERR_UNSUPPORTED;
   char buf[160];
-  if (c.variant2 >= 0)
+  if (c.variant2 >= 0 && (c.launch == tq::launch_tq2_skinny || c.launch == tq::launch_tq1_skinny))
+    snprintf(buf, sizeof buf, "%s<%d, %s>", c.name, c.variant, c.variant2 ? "true" : "false");
+  else if (c.variant2 >= 0)
     snprintf(buf, sizeof buf, "%s<%d, %d>", c.name, c.variant, c.variant2);
   else if (c.variant >= 0)
     snprintf(buf, sizeof buf, "%s<%d>", c.name, c.variant);

@@ -26,7 +26,14 @@ hipError_t launch_tq1_simple(const GemmArgs& a, hipStream_t stream);
 // Skinny MFMA kernels for M <= 16; skinny_rows(N) is the number of 16-row
 // groups one workgroup owns (the template argument of the kernel).
 int skinny_rows(int64_t N);
+int skinny_depth();                      // register ring depth (template argument)
+int skinny_stage(int64_t N, int64_t K);  // 1 when block scales are staged in LDS
 hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream);
+
+// TQ1 MFMA kernel: any M, in slices of 16 activation rows.
+hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream);
+int tq1_depth();
+int tq1_stage(int64_t N, int64_t K);
 
 // Tiled MFMA kernels for M > 16: a workgroup owns 16 mt activation rows x
 // 16 nr weight rows.

@@ -244,6 +244,14 @@ hipError_t launch_tq2_skinny_s(const GemmArgs& a, hipStream_t stream, int RG, in
 
 int skinny_rows(int64_t N) { return pick_rows(N, device_cus()); }
 
+int skinny_depth() { return kDepth; }
+
+int skinny_stage(int64_t N, int64_t K) {
+  const int64_t RG = skinny_rows(N);
+  const int64_t sbytes = ((16 * RG * (K / 256) * 2) + 15) & ~15;
+  return sbytes <= kScaleLdsMax ? 1 : 0;
+}
+
 hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream) {
   const int M = (int)a.M, K = (int)a.K;
   const int nb = K / 256;

@@ -93,8 +93,8 @@ SMALL = [(1, 1024, 1024), (2, 48, 512), (3, 100, 768), (4, 17, 256), (5, 64, 256
 @pytest.mark.parametrize("M,N,K", SMALL)
 def test_small_parity(fmt, path, M, N, K):
     need(fmt, path)
-    if path == "skinny" and M > SKINNY_MAX_M:
-        pytest.skip("the skinny family takes M <= 16")
+    if path == "skinny" and fmt == "tq2" and M > SKINNY_MAX_M:
+        pytest.skip("the TQ2 skinny family takes M <= 16")
     say(f"[small] {fmt} {path} M={M} N={N} K={K}")
     T, s = iid_problem(N, K, 0.31, 1)
     X = activations(M, K, 1)
@@ -109,7 +109,7 @@ def test_exact_special_cases(fmt, path):
     need(fmt, path)
     K = 512
     for M in (1, 5, 16, 40):
-        if path == "skinny" and M > SKINNY_MAX_M:
+        if path == "skinny" and fmt == "tq2" and M > SKINNY_MAX_M:
             continue
         say(f"[exact] {fmt} {path} M={M}")
         X = activations(M, K, 2)
