@@ -195,6 +195,34 @@ def gpu_bench(args):
     return calls, per_call, ms_step
 
 
+def kernel_source_sha():
+    """sha256 (first 16 hex) over the kernel sources, as recorded with the counters."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "bit_mixed_precision_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy of known size),
+    or None when there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != kernel_source_sha():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("traffic_bytes_per_launch")
+
+
 def roofline_of(per_call):
     """Roofline object for the kernel that takes the most time in the step."""
     by_kernel = {}
@@ -210,9 +238,11 @@ def roofline_of(per_call):
         achieved, peak, unit = nbytes / t / 1e9, HBM_PEAK / 1e9, "GB/s"
     else:
         achieved, peak, unit = flops / t / 1e12, MFMA_F16_PEAK / 1e12, "TFLOP/s"
+    traffic = recorded_traffic(dom)
     return {"kernel": dom, "bound": "hbm" if hbm_bound else "mfma",
             "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": None,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            "algorithmic_bytes_per_launch": round(nbytes / len(cs)),
             "launches_per_step": len(cs),
             "avg_launch_us": round(t / len(cs) * 1e6, 3)}
 
