@@ -65,7 +65,9 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
             if verbose and out.strip():
                 print(out)
     tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", *objs, "-o", tmp])
+    # -z defs: a kernel whose host stub was not emitted fails here, not at load time
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-Wl,-z,defs", *objs,
+          "-o", tmp])
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -57,6 +57,8 @@ struct Choice {
   const char* name;  // kernel template, as profilers list it
   int variant;       // first template argument, or -1 for none
   int variant2;      // second template argument, or -1 for none
+  int variant3 = -1;  // third and fourth template arguments, or -1 for none
+  int variant4 = -1;
 };
 
 constexpr int64_t kSkinnyMaxM = 16;
@@ -81,7 +83,7 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
     case TQ_PATH_TILED: {
       if (tq1) return Choice{nullptr, "", -1, -1};
       const tq::TiledShape t = tq::tiled_shape(M, N);
-      return Choice{tq::launch_tq2_tiled, "tq2_tiled_kernel", t.mt, t.nr};
+      return Choice{tq::launch_tq2_tiled, "tq2_tiled_kernel", t.mt, t.nr, t.ng, t.kg};
     }
     default:
       return Choice{nullptr, "", -1, -1};
@@ -159,6 +161,9 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
   char buf[160];
   if (c.variant2 >= 0 && (c.launch == tq::launch_tq2_skinny || c.launch == tq::launch_tq1_skinny))
     snprintf(buf, sizeof buf, "%s<%d, %s>", c.name, c.variant, c.variant2 ? "true" : "false");
+  else if (c.variant4 >= 0)
+    snprintf(buf, sizeof buf, "%s<%d, %d, %d, %d>", c.name, c.variant, c.variant2, c.variant3,
+             c.variant4);
   else if (c.variant2 >= 0)
     snprintf(buf, sizeof buf, "%s<%d, %d>", c.name, c.variant, c.variant2);
   else if (c.variant >= 0)

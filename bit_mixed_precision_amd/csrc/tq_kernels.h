@@ -35,10 +35,10 @@ hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream);
 int tq1_depth();
 int tq1_stage(int64_t N, int64_t K);
 
-// Tiled MFMA kernels for M > 16: a workgroup owns 16 mt activation rows x
-// 16 nr weight rows.
+// Tiled MFMA kernels for M > 16: a workgroup of 4 waves (ng weight-row
+// groups x kg k-groups) owns 16 mt activation rows x 16 nr ng weight rows.
 struct TiledShape {
-  int mt, nr;
+  int mt, nr, ng, kg;
 };
 TiledShape tiled_shape(int64_t M, int64_t N);
 hipError_t launch_tq2_tiled(const GemmArgs& a, hipStream_t stream);
