@@ -44,6 +44,7 @@ SIGNATURES = {
     "tq_kernel_name": (_I, [_I, _I64, _I64, _I64, _I, C.c_char_p, _I64]),
     "tq_gemm_tq2_ex": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "tq_gemm_tq1_ex": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _P]),
+    "tq_gemm_tq2_tiled": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -192,6 +193,16 @@ def tq_gemm_tq1_ex(X, qs, scales, path: int, Y=None, stream=None):
     Y = _out(Y, M, N, X)
     _check(lib.tq_gemm_tq1_ex(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K, path,
                               _stream(stream)), "tq_gemm_tq1")
+    return Y
+
+
+def tq_gemm_tq2_tiled(X, qs, scales, mt: int, ng: int, kg: int, Y=None, stream=None):
+    """tq_gemm_tq2 on the tiled kernel with an explicit (mt, ng, kg) tile."""
+    M, K = X.shape
+    N = qs.shape[0]
+    Y = _out(Y, M, N, X)
+    _check(lib.tq_gemm_tq2_tiled(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, ng, kg,
+                                 _stream(stream)), "tq_gemm_tq2_tiled")
     return Y
 
 

@@ -176,6 +176,19 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
   return TQ_OK;
 }
 
+int tq_gemm_tq2_tiled(const void* X, const void* qs, const void* scales, void* Y, int64_t M,
+                      int64_t N, int64_t K, int mt, int ng, int kg, void* stream) {
+  bool noop = false;
+  int st = check_gemm(X, qs, scales, Y, M, N, K, false, 0, &noop);
+  if (st != TQ_OK || noop) return st;
+  const tq::TiledShape t{mt, 4, ng, kg};
+  if (!tq::tiled_compiled(t)) return TQ_ERR_UNSUPPORTED;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  tq::GemmArgs a{X, qs, scales, Y, M, N, K, 0};
+  return finish(tq::launch_tq2_tiled_shape(t, a, static_cast<hipStream_t>(stream)));
+}
+
 int tq_gemm_tq2(const void* X, const void* qs, const void* scales, void* Y, int64_t M, int64_t N,
                 int64_t K, void* stream) {
   return tq_gemm_tq2_ex(X, qs, scales, Y, M, N, K, TQ_PATH_AUTO, stream);

@@ -41,6 +41,8 @@ struct TiledShape {
   int mt, nr, ng, kg;
 };
 TiledShape tiled_shape(int64_t M, int64_t N);
+bool tiled_compiled(const TiledShape& t);  // one of the instantiated tiles
 hipError_t launch_tq2_tiled(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_tq2_tiled_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream);
 
 }  // namespace tq

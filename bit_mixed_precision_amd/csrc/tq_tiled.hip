@@ -14,8 +14,10 @@
 //    consecutive lanes per row, so every request is a whole cache line.  The
 //    16-byte piece a lane fetches is XOR-swizzled on the global side, which
 //    lets the MFMA-order ds_read_b128 of 16 rows hit 16 distinct bank groups.
-//    A ring of kStages stages (64 k of every k-group's block each) keeps
-//    kStages - 1 stages in flight behind one barrier per stage;
+//    A ring of XS stages (64 k of every k-group's block each) keeps XS - 1
+//    stages in flight behind one barrier per stage; XS (3 to 6) and the
+//    weight ring depth WD (1 or 2 rounds) are the deepest that fit the LDS
+//    of one compute unit (8-wave workgroups) or half of it (4-wave ones);
 //  * weights and block scales take the same direct path a round ahead (16
 //    rows x 64 B per weight instruction, 4 lanes per row), so the loop holds
 //    no register loads and every wait is an explicit, exact vmcnt; a lane
@@ -32,6 +34,7 @@
 #include "tq_common.h"
 #include "tq_kernels.h"
 #include "tq_mfma.h"
+#include "tq_tiled_sched.h"
 
 namespace tq {
 namespace {
@@ -43,8 +46,6 @@ __device__ __forceinline__ void sfor(F&& f) {
     sfor<I + 1, N>(f);
   }
 }
-
-constexpr int kStages = 3;  // LDS ring depth (stages of 64 k)
 
 // s_waitcnt immediate that waits for the vector-memory counter only.
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
@@ -127,19 +128,31 @@ __device__ __forceinline__ void mem_clobber() { asm volatile("" ::: "memory"); }
 
 template <int MT, int NR, int NG, int KG>
 struct TileGeom {
-  static_assert(NG * KG == 4, "a workgroup is 4 waves");
+  static constexpr int WV = NG * KG;  // waves per workgroup
+  static_assert(WV == 4 || WV == 8, "a workgroup is 4 or 8 waves");
   static constexpr int BM = 16 * MT;
   static constexpr int BNW = 16 * NR;  // weight rows per wave
   static constexpr int BN = NG * BNW;
   static constexpr int kChunk = BM * 128;  // one k-group's stage: BM rows x 64 k
   static constexpr int kStage = KG * kChunk;
-  static constexpr int kRing = kStages * kStage;
-  static constexpr int kXfer = KG * BM / 8;  // DMA instructions per stage
-  static_assert(kXfer % 4 == 0, "DMA instructions split evenly over 4 waves");
-  static constexpr int kPer = kXfer / 4;
+  static constexpr int kWRound = WV * (NR * 1024 + 256);  // weights + scales of a round
+  // Ring depths: the deepest (XS, WD) whose rings fit the LDS budget.
+  static constexpr int kBudget = WV == 8 ? 160 * 1024 : 80 * 1024;
+  static constexpr RingPlan kPlan = ring_plan(kStage, kWRound, kBudget);
+  static constexpr int XS = kPlan.xs;
+  static constexpr int WD = kPlan.wd;
+  static_assert(XS <= 4 * WD - 1, "weights must arrive before the stage that reads them");
+  static_assert(XS <= 6, "round 0 is the only round whose wait window reaches the prologue");
+  static constexpr int kRing = XS * kStage;
+  static constexpr int RG8 = BM / 8;          // 8-row DMA groups per chunk
+  static constexpr int kXfer = KG * RG8;      // DMA instructions per stage
+  static_assert(kXfer % WV == 0, "DMA instructions split evenly over the waves");
+  static_assert(RG8 % WV == 0 || WV % RG8 == 0, "row groups map evenly to waves");
+  static constexpr int kPer = kXfer / WV;
+  static constexpr int RP = RG8 >= WV ? RG8 / WV : 1;  // distinct row groups per wave
   static constexpr int kWOff = kRing;             // weights: 1 KB per (wave, row group)
-  static constexpr int kSOff = kWOff + 4 * NR * 1024;  // scales: one dword per wave lane
-  static constexpr int kLoop = kSOff + 4 * 256;
+  static constexpr int kSOff = kWOff + WD * WV * NR * 1024;  // scales: a dword per lane
+  static constexpr int kLoop = kSOff + WD * WV * 256;
   static constexpr int kRed = (KG - 1) * NG * MT * NR * 256 * 4;
   static constexpr int kLds = kLoop > kRed ? kLoop : kRed;
   static_assert(NR == 4, "one scale DMA covers the 64 weight rows of a wave");
@@ -150,7 +163,7 @@ struct TileGeom {
 // different XCDs, and the m tiles of one weight-row tile run back to back on
 // the same XCD, so its weights are read from HBM once.
 template <int MT, int NR, int NG, int KG>
-__global__ __launch_bounds__(256) void tq2_tiled_kernel(const uint16_t* __restrict__ X,
+__global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(const uint16_t* __restrict__ X,
                                                         const uint8_t* __restrict__ qs,
                                                         const uint16_t* __restrict__ scales,
                                                         uint16_t* __restrict__ Y, int M, int N,
@@ -172,40 +185,41 @@ __global__ __launch_bounds__(256) void tq2_tiled_kernel(const uint16_t* __restri
   const int g = lane >> 4;
   const int nb = K >> 8;
   const int rounds = (nb + KG - 1) / KG;
-  const int S = 4 * rounds;  // stages (>= 4 > kStages - 1)
+  const int S = 4 * rounds;  // stages
   const size_t row_bytes = (size_t)(K >> 2);
 
   NaturalConsts dc;
   dc.init();
 
-  // ---- activation DMA: instruction q = wave + 4 u moves rows 8 rg .. 8 rg + 7
-  // of k-group c's chunk; lane i takes row 8 rg + i / 8, LDS piece i % 8, i.e.
-  // global piece (i % 8) ^ swz(row), swz(row) = (row / 2) % 8.  Rows past M
-  // read row m_base (valid data; never written).
-  const uint16_t* xsrc[G::kPer];
-  int xc[G::kPer];
-  uint32_t xdst[G::kPer];
+  // ---- activation DMA: instruction q = wave + WV u moves rows 8 rg .. 8 rg + 7
+  // (rg = q % RG8) of k-group c = q / RG8's chunk; lane i takes row
+  // 8 rg + i / 8, LDS piece i % 8, i.e. global piece (i % 8) ^ swz(row),
+  // swz(row) = (row / 2) % 8.  A wave touches only RP distinct row groups.
+  // Rows past M read row m_base (valid data; never written).
+  // Byte offsets from the tile's first activation row (< 64 rows x 2^21 B).
+  const unsigned char* xbase = reinterpret_cast<const unsigned char*>(X + (size_t)m_base * K);
+  uint32_t xoff[G::RP];
 #pragma unroll
-  for (int u = 0; u < G::kPer; ++u) {
-    const int q = wave + 4 * u;
-    const int c = q / (G::BM / 8);
-    const int rg = q % (G::BM / 8);
+  for (int p = 0; p < G::RP; ++p) {
+    const int rg = G::RG8 >= G::WV ? wave + G::WV * p : wave % G::RG8;
     const int row = 8 * rg + (lane >> 3);
     const int gp = (lane & 7) ^ ((row >> 1) & 7);
-    const int m = m_base + row < M ? m_base + row : m_base;
-    xsrc[u] = X + (size_t)m * K + 8 * gp;
-    xc[u] = c;
-    xdst[u] = c * G::kChunk + rg * 1024;
+    const int rel = m_base + row < M ? row : 0;
+    xoff[p] = (uint32_t)rel * (uint32_t)K * 2u + 16u * gp;
   }
   auto issue = [&](int s) {
     const int r = s >> 2;
     const int ch = s & 3;
-    const uint32_t slot = (uint32_t)(s % kStages) * G::kStage;
+    const uint32_t slot = (uint32_t)(s % G::XS) * G::kStage;
 #pragma unroll
     for (int u = 0; u < G::kPer; ++u) {
-      int b = r * KG + xc[u];
+      const int p = u % G::RP;
+      const int c = G::RG8 >= G::WV ? u / G::RP : wave / G::RG8 + u * (G::WV / G::RG8);
+      const int rg = G::RG8 >= G::WV ? wave + G::WV * p : wave % G::RG8;
+      int b = r * KG + c;
       b = b < nb ? b : nb - 1;
-      dma16(xsrc[u] + 256 * (size_t)b + 64 * ch, smem + slot + xdst[u]);
+      dma16(xbase + xoff[p] + (uint32_t)(512 * b + 128 * ch),
+            smem + slot + c * G::kChunk + rg * 1024);
     }
   };
 
@@ -215,41 +229,46 @@ __global__ __launch_bounds__(256) void tq2_tiled_kernel(const uint16_t* __restri
   // (i % 4) ^ ((row / 4) % 4).  The scale instruction gives lane i the scale of
   // the wave's row i (zero-extended into one LDS dword).  Rows past N read row
   // n_base (valid data; never written).
-  const uint8_t* wsrc[NR];
+  // 32-bit byte offsets from the workgroup's first row (the lowest row any
+  // lane reads) keep the addresses in few registers: a tile spans at most 256
+  // rows of K / 4 <= 2^18 bytes.
+  const uint8_t* wbase = qs + (size_t)n_base * row_bytes;
+  const uint16_t* sbase = scales + (size_t)n_base * nb;
+  uint32_t woff[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
     const int row = 16 * r + (lane >> 2);
     const int n = n_base + wn * G::BNW + row;
-    const int nn = n < N ? n : n_base;
+    const int rel = n < N ? n - n_base : 0;
     const int gp = (lane & 3) ^ ((row >> 2) & 3);
-    wsrc[r] = qs + (size_t)nn * row_bytes + 16 * gp;
+    woff[r] = (uint32_t)rel * (uint32_t)row_bytes + 16u * gp;
   }
-  const uint16_t* ssrc;
+  uint32_t soff;
   {
     const int n = n_base + wn * G::BNW + lane;
-    ssrc = scales + (size_t)(n < N ? n : n_base) * nb;
+    soff = (uint32_t)(n < N ? n - n_base : 0) * (uint32_t)nb * 2u;
   }
-  const uint32_t wdst = G::kWOff + wave * NR * 1024;
-  const uint32_t sdst = G::kSOff + wave * 256;
+  // Round rd's weights and scales sit in slot rd % WD of their rings.
+  auto wdst = [&](int rd) { return G::kWOff + ((rd % G::WD) * G::WV + wave) * NR * 1024; };
+  auto sdst = [&](int rd) { return G::kSOff + ((rd % G::WD) * G::WV + wave) * 256; };
   auto issue_w = [&](int rd) {
-    int b = rd * KG + wk;
+    const int rc = rd < rounds ? rd : rounds - 1;  // past the end: a harmless refill
+    int b = rc * KG + wk;
     b = b < nb ? b : nb - 1;
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
-      dma16(wsrc[r] + 64 * (size_t)b, smem + wdst + r * 1024);
-    dma2(ssrc + b, smem + sdst);
+    for (int r = 0; r < NR; ++r) dma16(wbase + woff[r] + 64 * b, smem + wdst(rd) + r * 1024);
+    dma2(reinterpret_cast<const unsigned char*>(sbase) + soff + 2 * b, smem + sdst(rd));
   };
   constexpr int kWIssue = NR + 1;  // DMA instructions of issue_w
   // Read-back offsets: lane (li, g) wants bytes 16 g .. 16 g + 15 of row
   // 16 r + li, and the scale of that row.
-  const uint32_t w_rd = wdst + li * 64 + 16 * (g ^ ((li >> 2) & 3));
-  const uint32_t s_rd = sdst + 4 * li;
+  const uint32_t w_rd = li * 64 + 16 * (g ^ ((li >> 2) & 3));
+  const uint32_t s_rd = 4 * li;
 
   // ds_read_b128 offsets of the A operand (row li of m-tile i at +2048 i):
   // step H of a stage needs global piece 4 H + g of row li.
-  uint32_t a_off[2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) a_off[h] = li * 128 + 16 * ((4 * h + g) ^ ((li >> 1) & 7));
+  // (4 + g) ^ swz = (g ^ swz) ^ 4 for g < 4, so step 1 is step 0's offset ^ 64.
+  const uint32_t a_off0 = li * 128 + 16 * (g ^ ((li >> 1) & 7));
 
   float4v C[MT][NR];
 #pragma unroll
@@ -257,58 +276,101 @@ __global__ __launch_bounds__(256) void tq2_tiled_kernel(const uint16_t* __restri
 #pragma unroll
     for (int r = 0; r < NR; ++r) C[i][r] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 wb[NR];
-  uint32_t s2[NR];
-
-  issue_w(0);
+  // Weights of round rd in B order and their scale pairs; a k-group without a
+  // block in the round (K / 256 not a multiple of KG) gets scale 0, so its
+  // MFMAs add nothing and every wave runs the same straight-line code.
+  auto read_w = [&](int rd, u32x4* wbo, uint32_t* s2o) {
+    const bool active = rd * KG + wk < nb;
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue(s);
+    for (int r = 0; r < NR; ++r) {
+      wbo[r] = to_b_order(*reinterpret_cast<const u32x4*>(smem + wdst(rd) + w_rd + r * 1024));
+      const uint32_t sc = *reinterpret_cast<const uint32_t*>(smem + sdst(rd) + s_rd + 64 * r);
+      s2o[r] = active ? (sc | (sc << 16)) : 0u;
+    }
+  };
+
+  u32x4 wb[NR], wnx[NR];
+  uint32_t s2[NR], s2n[NR];
+  half8 Bc[NR];  // B operands of the coming stage's first step
+
+#pragma unroll
+  for (int rd = 0; rd < G::WD; ++rd) issue_w(rd);
+#pragma unroll
+  for (int s = 0; s < G::XS - 1; ++s) issue(s < S ? s : S - 1);
+  // The wave's own round-0 weights (its oldest DMA) must have landed.
+  mem_clobber();
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm((G::WD - 1) * kWIssue + (G::XS - 1) * G::kPer));
+  mem_clobber();
+  read_w(0, wb, s2);
+#pragma unroll
+  for (int r = 0; r < NR; ++r) Bc[r] = dc.operand<0>(wb[r][0], s2[r]);
 
   for (int rd = 0; rd < rounds; ++rd) {
-    const bool active = rd * KG + wk < nb;  // wave-uniform
     sfor<0, 4>([&](auto cc) {
       constexpr int ch = decltype(cc)::value;
       const int s = 4 * rd + ch;
-      // Stage s's DMA came kStages - 1 = 2 iterations ago; younger are the
-      // next stage's DMA and, when ch = 1 fell in between (ch = 2, 3), the
-      // weight/scale DMA issued after it.  The weight/scale DMA of round rd
-      // is older than stage s's, so ch = 0 finds it complete as well.
-      static_assert(kStages == 3, "the count below assumes a 3-stage ring");
-      constexpr int younger = G::kPer + (ch >= 2 ? kWIssue : 0);
+      // Stage s's DMA came XS - 1 iterations ago and is the last DMA of its
+      // iteration; younger are the activation DMAs of the XS - 2 iterations
+      // after it and the weight/scale DMA of those among them with ch = 1
+      // (issued first in its iteration).  Round rd + 1's weights, read at
+      // ch = 3, are older than stage 4 rd + 3's DMA (XS <= 4 WD - 1).
       mem_clobber();
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(younger));
+      if (rd == 0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_younger(G::XS, G::kPer, kWIssue, ch, true)));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_younger(G::XS, G::kPer, kWIssue, ch, false)));
       __builtin_amdgcn_s_barrier();
       mem_clobber();
-      if constexpr (ch == 0) {
+      const unsigned char* base = smem + (uint32_t)(s % G::XS) * G::kStage + wk * G::kChunk;
+      half8 A[2][MT];
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          wb[r] = to_b_order(*reinterpret_cast<const u32x4*>(smem + w_rd + r * 1024));
-          const uint32_t sc = *reinterpret_cast<const uint32_t*>(smem + s_rd + 64 * r);
-          s2[r] = sc | (sc << 16);
-        }
-      }
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+          A[h][i] = *reinterpret_cast<const half8*>(base + (a_off0 ^ (64u * h)) + 2048 * i);
+      if constexpr (ch == 3) read_w(rd + 1, wnx, s2n);  // stale refill past the end
+      // all LDS reads of the stage are in flight before any of them is used
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (ch == 1) issue_w(rd + G::WD);  // its slot held round rd, read at
+      // ch = 3 of the round before
       {
-        const int sn = s + kStages - 1;
+        const int sn = s + G::XS - 1;
         issue(sn < S ? sn : S - 1);  // past the end: a harmless refill
       }
-      if constexpr (ch == 1) issue_w(rd + 1 < rounds ? rd + 1 : rd);  // after this
-      // wave's ch = 0 reads of the buffers, which the barrier above ordered
-      if (active) {
-        const unsigned char* base =
-            smem + (uint32_t)(s % kStages) * G::kStage + wk * G::kChunk;
-        sfor<0, 2>([&](auto hh) {
-          constexpr int H = decltype(hh)::value;
-          half8 B[NR];
+      __builtin_amdgcn_sched_barrier(0);
+      // step 0 with the operands decoded one stage earlier, while step 1's
+      // operands are decoded; then step 1 while the next stage's step 0 is
+      half8 B1[NR];
 #pragma unroll
-          for (int r = 0; r < NR; ++r) B[r] = dc.operand<H>(wb[r][ch], s2[r]);
+      for (int r = 0; r < NR; ++r) B1[r] = dc.operand<1>(wb[r][ch], s2[r]);
 #pragma unroll
-          for (int i = 0; i < MT; ++i) {
-            const half8 A = *reinterpret_cast<const half8*>(base + a_off[H] + 2048 * i);
+      for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int r = 0; r < NR; ++r) C[i][r] = mfma16(A, B[r], C[i][r]);
-          }
-        });
+        for (int r = 0; r < NR; ++r) C[i][r] = mfma16(A[0][i], Bc[r], C[i][r]);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        if constexpr (ch < 3)
+          Bc[r] = dc.operand<0>(wb[r][ch + 1], s2[r]);
+        else
+          Bc[r] = dc.operand<0>(wnx[r][0], s2n[r]);
       }
+#pragma unroll
+      for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int r = 0; r < NR; ++r) C[i][r] = mfma16(A[1][i], B1[r], C[i][r]);
+      if constexpr (ch == 3) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          wb[r] = wnx[r];
+          s2[r] = s2n[r];
+        }
+      }
+      // Issue order: one MFMA, then up to four decode instructions, so the
+      // matrix core and the vector ALU work side by side.
+      sfor<0, 2 * MT * NR>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      });
     });
   }
 
@@ -342,6 +404,7 @@ __global__ __launch_bounds__(256) void tq2_tiled_kernel(const uint16_t* __restri
           const int m = m_base + 16 * i + 4 * g + e;
           if (m < M && n < N) Y[(size_t)m * N + n] = f2h_bits(sum);
         }
+        __builtin_amdgcn_sched_barrier(0);  // one tile's partial sums at a time
       }
     }
   }
@@ -363,7 +426,8 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
   const int64_t groups = (n_tiles + 7) / 8;
   const int64_t wgs = groups * 8 * m_tiles;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((tq2_tiled_kernel<MT, NR, NG, KG>), dim3((unsigned)wgs), dim3(256), G::kLds,
+  hipLaunchKernelGGL((tq2_tiled_kernel<MT, NR, NG, KG>), dim3((unsigned)wgs), dim3(64 * G::WV),
+                     G::kLds,
                      stream, static_cast<const uint16_t*>(a.X),
                      static_cast<const uint8_t*>(a.qs), static_cast<const uint16_t*>(a.scales),
                      static_cast<uint16_t*>(a.Y), (int)a.M, (int)a.N, (int)a.K, (int)n_tiles,
@@ -373,27 +437,48 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
 
 }  // namespace
 
-// Tile choice: 32 activation rows per tile up to M = 32, else 64; two
-// weight-row groups x two k-groups (BN = 128) when that still gives one
-// workgroup per compute unit, else one weight-row group x four k-groups
-// (BN = 64).
+// Tile choice (measured at K = 8192, N = 8192 and 28672, M = 17..128).  A
+// stage costs a wave about the same whatever the tile, so what counts is the
+// number of stages a workgroup runs (fewer with more k-groups) and how many
+// compute units have one.  The 8-wave tiles (one workgroup per compute unit,
+// half the activation re-reads) win once they alone fill about 85% of the
+// compute units: 64 x 256 (4 row groups x 2 k-groups) past M = 64, 64 x 128
+// (2 x 4) up to M = 64.  Below that the 4-wave tile of 1 row group x 4
+// k-groups (BN = 64, twice the workgroups), with 32 activation rows up to
+// M = 64 so that the activation-row tiles spread over more compute units.
 TiledShape tiled_shape(int64_t M, int64_t N) {
   const int64_t cus = device_cus();
-  const int mt = M <= 32 ? 2 : 4;
-  const int64_t m_tiles = (M + 16 * mt - 1) / (16 * mt);
-  const int64_t wide = ((N + 127) / 128) * m_tiles;
-  if (wide >= cus) return TiledShape{mt, 4, 2, 2};
-  return TiledShape{mt, 4, 1, 4};
+  if (M > 32) {
+    const bool wide = M > 64;
+    const TiledShape t8 = wide ? TiledShape{4, 4, 4, 2} : TiledShape{4, 4, 2, 4};
+    const int64_t bn = 16 * 4 * t8.ng;
+    const int64_t wgs = ((N + bn - 1) / bn) * ((M + 63) / 64);
+    if (20 * wgs >= 17 * cus) return t8;
+    return wide ? TiledShape{4, 4, 1, 4} : TiledShape{2, 4, 1, 4};
+  }
+  return TiledShape{2, 4, 1, 4};
+}
+
+template <int MT>
+hipError_t launch_mt(const TiledShape& t, const GemmArgs& a, hipStream_t stream) {
+  if (t.ng == 4) return launch_tiled<MT, 4, 4, 2>(a, stream);
+  if (t.kg == 4) return t.ng == 2 ? launch_tiled<MT, 4, 2, 4>(a, stream)
+                                  : launch_tiled<MT, 4, 1, 4>(a, stream);
+  return launch_tiled<MT, 4, 2, 2>(a, stream);
+}
+
+bool tiled_compiled(const TiledShape& t) {
+  if ((t.mt != 2 && t.mt != 4) || t.nr != 4) return false;
+  return (t.ng == 4 && t.kg == 2) || (t.ng == 2 && t.kg == 4) || (t.ng == 2 && t.kg == 2) ||
+         (t.ng == 1 && t.kg == 4);
+}
+
+hipError_t launch_tq2_tiled_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream) {
+  return t.mt == 2 ? launch_mt<2>(t, a, stream) : launch_mt<4>(t, a, stream);
 }
 
 hipError_t launch_tq2_tiled(const GemmArgs& a, hipStream_t stream) {
-  const TiledShape t = tiled_shape(a.M, a.N);
-  if (t.mt == 2) {
-    if (t.ng == 2) return launch_tiled<2, 4, 2, 2>(a, stream);
-    return launch_tiled<2, 4, 1, 4>(a, stream);
-  }
-  if (t.ng == 2) return launch_tiled<4, 4, 2, 2>(a, stream);
-  return launch_tiled<4, 4, 1, 4>(a, stream);
+  return launch_tq2_tiled_shape(tiled_shape(a.M, a.N), a, stream);
 }
 
 }  // namespace tq

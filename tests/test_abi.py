@@ -78,6 +78,19 @@ def test_gemm_argument_errors():
     assert tq.raw_call("tq_gemm_tq2", None, None, None, None, 0, 5, 256, None) == tq.TQ_OK
 
 
+def _gt(mt, ng, kg, X=A, M=40, K=512):
+    return tq.raw_call("tq_gemm_tq2_tiled", X, A, A, A, M, 64, K, mt, ng, kg, None)
+
+
+def test_tiled_tile_errors():
+    # argument checks first, then the tile, both before any device work
+    assert _gt(4, 2, 2, X=None) == tq.TQ_ERR_NULL
+    assert _gt(4, 2, 2, K=300) == tq.TQ_ERR_SHAPE
+    for tile in [(3, 2, 2), (4, 4, 4), (2, 1, 8), (4, 8, 1), (0, 2, 2), (4, 1, 2)]:
+        assert _gt(*tile) == tq.TQ_ERR_UNSUPPORTED, tile
+    assert _gt(3, 2, 2, X=None, M=0) == tq.TQ_OK
+
+
 @pytest.mark.skipif(HAS_GPU, reason="checks the no-device error; a GPU is present")
 def test_gemm_without_device():
     assert _g2() == tq.TQ_ERR_DEVICE

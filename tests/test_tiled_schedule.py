@@ -1,0 +1,130 @@
+"""The tiled TQ2 kernel's DMA schedule (tq_tiled_sched.h), checked on the CPU.
+
+The kernel keeps activations, weights and scales flowing into LDS with
+global_load_lds and waits for them with explicit s_waitcnt vmcnt(n) counts; a
+count that is too large reads LDS before the data lands.  This test compiles
+the header's constexpr arithmetic with g++, then replays the kernel's issue
+order instruction by instruction for every compiled tile and several round
+counts, and checks that each wait covers the data its stage reads.
+"""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "bit_mixed_precision_amd", "csrc")
+
+# (MT, NG, KG) of the compiled tiles; NR = 4 weight-row groups per wave.
+TILES = [(mt, ng, kg) for mt in (2, 4) for ng, kg in ((4, 2), (2, 4), (2, 2), (1, 4))]
+NR = 4
+W_ISSUE = NR + 1  # weight DMAs plus one scale DMA per round
+
+DRIVER = r"""
+#include <cstdio>
+#include "tq_tiled_sched.h"
+int main() {
+  const int tiles[8][3] = {%s};
+  for (const auto& t : tiles) {
+    const int mt = t[0], ng = t[1], kg = t[2], wv = ng * kg;
+    const int stage = kg * 16 * mt * 128, round = wv * (%d * 1024 + 256);
+    const int budget = wv == 8 ? 160 * 1024 : 80 * 1024;
+    const tq::RingPlan p = tq::ring_plan(stage, round, budget);
+    const int kper = kg * 2 * mt / wv;
+    std::printf("%%d %%d %%d %%d %%d %%d", mt, ng, kg, p.xs, p.wd, kper);
+    for (int r0 = 1; r0 >= 0; --r0)
+      for (int ch = 0; ch < 4; ++ch) std::printf(" %%d", tq::vm_younger(p.xs, kper, %d, ch, r0));
+    std::printf("\n");
+  }
+}
+"""
+
+
+@pytest.fixture(scope="module")
+def plans(tmp_path_factory):
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    d = tmp_path_factory.mktemp("sched")
+    src = d / "drv.cpp"
+    src.write_text(DRIVER % (", ".join("{%d, %d, %d}" % t for t in TILES), NR, W_ISSUE))
+    exe = d / "drv"
+    subprocess.run([gxx, "-std=c++17", "-O1", f"-I{CSRC}", str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    rows = {}
+    for line in out.strip().splitlines():
+        v = [int(x) for x in line.split()]
+        mt, ng, kg, xs, wd, kper = v[:6]
+        rows[(mt, ng, kg)] = dict(xs=xs, wd=wd, kper=kper, r0=v[6:10], rn=v[10:14])
+    assert set(rows) == set(TILES)
+    return rows
+
+
+def replay(xs, wd, kper, r0, rn, rounds):
+    """Issue order of one wave; returns the first uncovered read, else None."""
+    q = []  # (kind, id)
+    for rd in range(wd):
+        q += [("W", rd)] * W_ISSUE
+    S = 4 * rounds
+    for s in range(xs - 1):
+        q += [("X", min(s, S - 1))] * kper
+    for rd in range(rounds):
+        for ch in range(4):
+            s = 4 * rd + ch
+            n = (r0 if rd == 0 else rn)[ch]
+            landed = len(q) - n  # instructions 0 .. landed-1 have completed
+            # every instruction of stage s's first issue (later ones past the
+            # end refill the same bytes)
+            group = [i for i, e in enumerate(q) if e == ("X", s)][:kper]
+            if max(group) >= landed:
+                return ("X", rd, ch)
+            if ch == 3:  # the next round's weights are read here
+                last_w = max(i for i, e in enumerate(q) if e == ("W", rd + 1))
+                if last_w >= landed:
+                    return ("W", rd, ch)
+            if ch == 1:
+                q += [("W", rd + wd)] * W_ISSUE
+            q += [("X", min(s + xs - 1, S - 1))] * kper
+    return None
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_every_wait_covers_its_data(plans, tile):
+    p = plans[tile]
+    assert 3 <= p["xs"] <= 6 and p["wd"] in (1, 2) and p["xs"] <= 4 * p["wd"] - 1
+    for rounds in (1, 2, 3, 5, 8, 32):
+        assert replay(p["xs"], p["wd"], p["kper"], p["r0"], p["rn"], rounds) is None, (tile, rounds)
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_ring_fits_lds(plans, tile):
+    mt, ng, kg = tile
+    p, wv = plans[tile], ng * kg
+    ring = p["xs"] * kg * 16 * mt * 128 + p["wd"] * wv * (NR * 1024 + 256)
+    red = (kg - 1) * ng * mt * NR * 256 * 4
+    budget = 160 * 1024 if wv == 8 else 80 * 1024
+    assert max(ring, red) <= 160 * 1024
+    if ring <= budget:  # the plan is the deepest candidate that fits
+        deeper = [(x, w) for x, w in ((6, 2), (5, 2), (4, 2), (3, 2), (3, 1))
+                  if x * kg * 16 * mt * 128 + w * wv * (NR * 1024 + 256) <= budget]
+        assert (p["xs"], p["wd"]) == deeper[0]
+
+
+def test_a_count_one_too_large_is_caught(plans):
+    """Mutation check of the replay itself: raising any single wait count by one
+    (waiting for one instruction less) must leave some read uncovered in some tile."""
+    caught = 0
+    for tile in TILES:
+        p = plans[tile]
+        for which in ("r0", "rn"):
+            for ch in range(4):
+                bad = dict(p)
+                bad[which] = list(p[which])
+                bad[which][ch] += 1
+                if any(replay(bad["xs"], bad["wd"], bad["kper"], bad["r0"], bad["rn"], r)
+                       for r in (1, 2, 3, 8)):
+                    caught += 1
+    # every count of every tile is tight
+    assert caught == len(TILES) * 8
