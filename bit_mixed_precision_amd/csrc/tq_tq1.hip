@@ -58,7 +58,11 @@ __device__ constexpr int kByteOfSlot[8] = {0, 2, 1, 3, 4, 6, 5, 7};
 // Stages the activations of spans [u0, u0 + nu) for rows m_base .. m_base + mrows - 1
 // into LDS in decoder order: for every (m, span u, group g, operand o) 8 halves.
 // o < 5: plain X at the operand's weights (zero past K); o >= 5: the same
-// masked to the weights at or past the span's block boundary.
+// masked to the weights at or past the span's block boundary.  A unit (m, u, g)
+// covers the 40 consecutive activations k0 = 160 u + 40 g .. k0 + 39: five
+// coalesced 16-byte loads (K and k0 are multiples of 8, so a chunk is either
+// wholly inside the row or wholly past K), then every operand dword is one
+// v_perm_b32 of two loaded dwords.
 __device__ void tq1_stage_x(unsigned char* xs, const uint16_t* __restrict__ X, int mrows,
                             int m_base, int K, int u0, int nu, int xstride) {
   const int units = mrows * nu * 4;
@@ -66,29 +70,47 @@ __device__ void tq1_stage_x(unsigned char* xs, const uint16_t* __restrict__ X, i
     const int g = q & 3;
     const int u = (q >> 2) % nu;
     const int m = (q >> 2) / nu;
-    const int k0 = 160 * (u0 + u);
-    const int kb = (k0 / 256 + 1) * 256;  // first block boundary after the span start
+    const int k0 = 160 * (u0 + u) + 40 * g;
+    const int kb = ((160 * (u0 + u)) / 256 + 1) * 256;  // first block boundary of the span
     const uint16_t* xrow = X + (size_t)(m_base + m) * K;
+    uint32_t e[20];  // activations k0 .. k0 + 39, two per dword
+#pragma unroll
+    for (int c = 0; c < 5; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (k0 + 8 * c + 8 <= K) v = *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * c);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) e[4 * c + t] = v[t];
+    }
     unsigned char* dst = xs + m * xstride + u * kSpanBytes + g * kUnitBytes;
+    // activations below lim (relative to k0) fall before the block boundary
+    const int lim = kb - k0;
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
-      uint32_t plain[4], masked[4];
+      uint32_t plain[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        uint32_t hv[2], mv[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int k = k0 + 40 * g + 5 * kByteOfSlot[2 * t + h] + j;
-          const uint32_t v = k < K ? (uint32_t)xrow[k] : 0u;
-          hv[h] = v;
-          mv[h] = k >= kb ? v : 0u;
-        }
-        plain[t] = hv[0] | (hv[1] << 16);
-        masked[t] = mv[0] | (mv[1] << 16);
+        // slot pair (2t, 2t + 1) holds activations a = 5 byte(2t) + j, b = 5 byte(2t+1) + j
+        const int a = 5 * kByteOfSlot[2 * t] + j;
+        const int b = 5 * kByteOfSlot[2 * t + 1] + j;
+        const uint32_t sel = ((b & 1) ? 0x07060000u : 0x05040000u) | ((a & 1) ? 0x0302u : 0x0100u);
+        plain[t] = perm(e[b >> 1], e[a >> 1], sel);
       }
       *reinterpret_cast<u32x4*>(dst + 16 * j) = u32x4{plain[0], plain[1], plain[2], plain[3]};
-      *reinterpret_cast<u32x4*>(dst + 16 * (5 + j)) =
-          u32x4{masked[0], masked[1], masked[2], masked[3]};
+      u32x4 masked;
+      if (lim <= 0) {
+        masked = u32x4{plain[0], plain[1], plain[2], plain[3]};
+      } else if (lim >= 40) {
+        masked = u32x4{0u, 0u, 0u, 0u};
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int a = 5 * kByteOfSlot[2 * t] + j;
+          const int b = 5 * kByteOfSlot[2 * t + 1] + j;
+          const uint32_t keep = (a >= lim ? 0x0000FFFFu : 0u) | (b >= lim ? 0xFFFF0000u : 0u);
+          masked[t] = plain[t] & keep;
+        }
+      }
+      *reinterpret_cast<u32x4*>(dst + 16 * (5 + j)) = masked;
     }
   }
 }
