@@ -76,7 +76,7 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
     case TQ_PATH_SKINNY:
       if (tq1)
         return Choice{tq::launch_tq1_skinny, "tq1_skinny_kernel", tq::tq1_depth(),
-                      tq::tq1_stage(N, K)};
+                      tq::tq1_stage(N, K), tq::tq1_slices(M)};
       if (M > kSkinnyMaxM) return Choice{nullptr, "", -1, -1};
       return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_depth(),
                     tq::skinny_stage(N, K)};
@@ -159,7 +159,10 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
   Choice c = choose(format == 1, M, N, K, path);
   if (!c.launch) return TQ_ERR_UNSUPPORTED;
   char buf[160];
-  if (c.variant2 >= 0 && (c.launch == tq::launch_tq2_skinny || c.launch == tq::launch_tq1_skinny))
+  if (c.launch == tq::launch_tq1_skinny)
+    snprintf(buf, sizeof buf, "%s<%d, %s, %d>", c.name, c.variant, c.variant2 ? "true" : "false",
+             c.variant3);
+  else if (c.variant2 >= 0 && c.launch == tq::launch_tq2_skinny)
     snprintf(buf, sizeof buf, "%s<%d, %s>", c.name, c.variant, c.variant2 ? "true" : "false");
   else if (c.variant4 >= 0)
     snprintf(buf, sizeof buf, "%s<%d, %d, %d, %d>", c.name, c.variant, c.variant2, c.variant3,

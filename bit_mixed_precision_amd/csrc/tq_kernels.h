@@ -34,6 +34,7 @@ hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream);
 int tq1_depth();
 int tq1_stage(int64_t N, int64_t K);
+int tq1_slices(int64_t M);  // 16-row activation slices per workgroup (template argument)
 
 // Tiled MFMA kernels for M > 16: a workgroup of 4 waves (ng weight-row
 // groups x kg k-groups) owns 16 mt activation rows x 16 nr ng weight rows.

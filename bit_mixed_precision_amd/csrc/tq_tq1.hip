@@ -135,7 +135,7 @@ struct Tq1Decoder {
   }
 };
 
-template <int D, bool STAGE>
+template <int D, bool STAGE, int MS>
 __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ qs, int ldq,
     const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int M, int N, int K, int RG,
@@ -150,8 +150,8 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
   const int wk = wave % WK;
   const int n_base = blockIdx.x * (16 * RG);
   const int rows = min(16 * RG, N - n_base);
-  const int m_base = blockIdx.y * 16;
-  const int mrows = min(16, M - m_base);
+  const int m_base = blockIdx.y * 16 * MS;  // MS slices of 16 activation rows
+  const int mrows = min(16 * MS, M - m_base);
   const int groups = (K + 4) / 5;
   const int nu = (groups + 31) / 32;  // 32-byte spans holding real bytes
   const int xstride = nuw * kSpanBytes + kPad;
@@ -167,9 +167,18 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     const uint16_t* src = scales + (size_t)n_base * nb;
     for (int i = threadIdx.x; i < rows * nb; i += blockDim.x) sc_lds[i] = src[i];
   }
-  const unsigned char* xa = smem + (li < mrows ? li : mrows - 1) * xstride + g * kUnitBytes;
+  // Activation row of this lane in slice ms (rows past M repeat the last one;
+  // their results are never written).
+  const unsigned char* xa[MS];
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) {
+    const int m = 16 * ms + li < mrows ? 16 * ms + li : mrows - 1;
+    xa[ms] = smem + m * xstride + g * kUnitBytes;
+  }
 
-  float4v acc = {0.f, 0.f, 0.f, 0.f};
+  float4v acc[MS];
+#pragma unroll
+  for (int ms = 0; ms < MS; ++ms) acc[ms] = float4v{0.f, 0.f, 0.f, 0.f};
   u32x2 wbuf[D];
 
   // The last span may reach past the row's ldq bytes; such bytes only hold
@@ -189,23 +198,47 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     // bytes (0, 2), (1, 3), (4, 6), (5, 7) of the lane's 8 bytes, one per half
     uint32_t q[4] = {w[0] & 0x00FF00FFu, (w[0] >> 8) & 0x00FF00FFu, w[1] & 0x00FF00FFu,
                      (w[1] >> 8) & 0x00FF00FFu};
-    const unsigned char* xb = xa + uw * kSpanBytes;
-    float4v Ca = {0.f, 0.f, 0.f, 0.f}, Cb = {0.f, 0.f, 0.f, 0.f};
-    sfor1<0, 5>([&](auto jj) {
-      constexpr int j = decltype(jj)::value;
-      u32x4 b;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) b[i] = dc.step(q[i]);
-      const half8 B = __builtin_bit_cast(half8, b);
-      const half8 A = *reinterpret_cast<const half8*>(xb + 16 * j);
-      const half8 Am = *reinterpret_cast<const half8*>(xb + 16 * (5 + j));
-      Ca = mfma16(A, B, Ca);
-      Cb = mfma16(Am, B, Cb);
-    });
     const int ba = (160 * u) >> 8;
     const float sa = scale_at(ba < nb ? ba : nb - 1);
-    const float sb = ba + 1 < nb ? scale_at(ba + 1) : sa;
-    acc += sa * Ca + (sb - sa) * Cb;
+    // A span holds a block boundary (and a second scale) only when the next
+    // block starts before the span ends; otherwise the masked product is zero.
+    const bool split = 256 * (ba + 1) < 160 * (u + 1) && ba + 1 < nb;  // wave-uniform
+    auto run = [&](auto with_b) {
+      constexpr bool WB = decltype(with_b)::value;
+      float4v Ca[MS], Cb[MS];
+#pragma unroll
+      for (int ms = 0; ms < MS; ++ms) Ca[ms] = Cb[ms] = float4v{0.f, 0.f, 0.f, 0.f};
+      uint32_t qq[4] = {q[0], q[1], q[2], q[3]};
+      sfor1<0, 5>([&](auto jj) {
+        constexpr int j = decltype(jj)::value;
+        u32x4 b;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) b[i] = dc.step(qq[i]);
+        const half8 B = __builtin_bit_cast(half8, b);  // decoded once, used by every slice
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) {
+          const unsigned char* xb = xa[ms] + uw * kSpanBytes;
+          const half8 A = *reinterpret_cast<const half8*>(xb + 16 * j);
+          Ca[ms] = mfma16(A, B, Ca[ms]);
+          if constexpr (WB) {
+            const half8 Am = *reinterpret_cast<const half8*>(xb + 16 * (5 + j));
+            Cb[ms] = mfma16(Am, B, Cb[ms]);
+          }
+        }
+      });
+      if constexpr (WB) {
+        const float sb = scale_at(ba + 1);
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) acc[ms] += sa * Ca[ms] + (sb - sa) * Cb[ms];
+      } else {
+#pragma unroll
+        for (int ms = 0; ms < MS; ++ms) acc[ms] += sa * Ca[ms];
+      }
+    };
+    if (split)
+      run(std::true_type{});
+    else
+      run(std::false_type{});
   };
 
   for (int u0 = 0; u0 < nu; u0 += nuw) {
@@ -229,18 +262,22 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
 
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
+  const int nw = RG * WK;  // waves of the workgroup
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave * 256 + i * 64 + lane] = acc[i];
+  for (int ms = 0; ms < MS; ++ms)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(ms * nw + wave) * 256 + i * 64 + lane] = acc[ms][i];
   __syncthreads();
-  for (int t = threadIdx.x; t < RG * 256; t += blockDim.x) {
-    const int r = t >> 8;
+  for (int t = threadIdx.x; t < MS * RG * 256; t += blockDim.x) {
+    const int ms = t / (RG * 256);
+    const int r = (t >> 8) % RG;
     const int e = t & 255;
     const int l = e & 63;
-    const int m = 4 * (l >> 4) + (e >> 6);
+    const int m = 16 * ms + 4 * (l >> 4) + (e >> 6);
     const int n = 16 * r + (l & 15);
     if (m < mrows && n < rows) {
       float sum = 0.f;
-      for (int k = 0; k < WK; ++k) sum += red[(r * WK + k) * 256 + e];
+      for (int k = 0; k < WK; ++k) sum += red[(ms * nw + r * WK + k) * 256 + e];
       Y[(size_t)(m_base + m) * N + n_base + n] = f2h_bits(sum);
     }
   }
@@ -248,18 +285,18 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
 
 constexpr int kDepth1 = 3;
 
-template <bool STAGE>
+template <bool STAGE, int MS>
 hipError_t launch_tq1_s(const GemmArgs& a, hipStream_t stream, dim3 grid, int W, int lds, int RG,
                         int WK, int nuw, int xregion) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(tq1_skinny_kernel<kDepth1, STAGE>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(tq1_skinny_kernel<kDepth1, STAGE, MS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((tq1_skinny_kernel<kDepth1, STAGE>), grid, dim3(64 * W), lds, stream,
+  hipLaunchKernelGGL((tq1_skinny_kernel<kDepth1, STAGE, MS>), grid, dim3(64 * W), lds, stream,
                      static_cast<const uint16_t*>(a.X), static_cast<const uint8_t*>(a.qs),
                      (int)a.ldq, static_cast<const uint16_t*>(a.scales),
                      static_cast<uint16_t*>(a.Y), (int)a.M, (int)a.N, (int)a.K, RG, WK, nuw,
@@ -267,9 +304,18 @@ hipError_t launch_tq1_s(const GemmArgs& a, hipStream_t stream, dim3 grid, int W,
   return hipGetLastError();
 }
 
+template <bool STAGE>
+hipError_t launch_tq1_ms(int ms, const GemmArgs& a, hipStream_t stream, dim3 grid, int W, int lds,
+                         int RG, int WK, int nuw, int xregion) {
+  if (ms == 2) return launch_tq1_s<STAGE, 2>(a, stream, grid, W, lds, RG, WK, nuw, xregion);
+  return launch_tq1_s<STAGE, 1>(a, stream, grid, W, lds, RG, WK, nuw, xregion);
+}
+
 }  // namespace
 
 int tq1_depth() { return kDepth1; }
+
+int tq1_slices(int64_t M) { return M <= 16 ? 1 : 2; }
 
 int tq1_stage(int64_t N, int64_t K) {
   const int64_t RG = skinny_rows(N);
@@ -287,20 +333,26 @@ hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream) {
   if (WK > nu) WK = nu;
   if (WK < 1) WK = 1;
   const int W = RG * WK;
-  const int mrows = M < 16 ? M : 16;
+  // Activation slices per workgroup: every weight is decoded once per
+  // workgroup, so a workgroup takes up to 32 activation rows (more rows give
+  // no gain: past that the activation reads from LDS, one per MFMA, bound it,
+  // and the 1024-thread workgroup runs out of registers).
+  const int ms = tq1_slices(M);
+  const int mrows = M < 16 * ms ? M : 16 * ms;
   int nuw = (kXLds / mrows - kPad) / kSpanBytes;
   if (nuw > nu) nuw = nu;
   if (nuw < 1) nuw = 1;
   const int xbytes = mrows * (nuw * kSpanBytes + kPad);
-  int xregion = xbytes > W * 1024 ? xbytes : W * 1024;
+  const int rbytes = ms * W * 1024;  // the partial sums reuse the window
+  int xregion = xbytes > rbytes ? xbytes : rbytes;
   xregion = (xregion + 15) & ~15;
   const int sbytes = ((16 * RG * nb * 2) + 15) & ~15;
   const bool stage = sbytes <= kScLds;
   const int lds = xregion + (stage ? sbytes : 0);
   if (lds > kLdsMax) return hipErrorInvalidValue;
-  dim3 grid((unsigned)((a.N + 16 * RG - 1) / (16 * RG)), (unsigned)((a.M + 15) / 16));
-  return stage ? launch_tq1_s<true>(a, stream, grid, W, lds, RG, WK, nuw, xregion)
-               : launch_tq1_s<false>(a, stream, grid, W, lds, RG, WK, nuw, xregion);
+  dim3 grid((unsigned)((a.N + 16 * RG - 1) / (16 * RG)), (unsigned)((a.M + 16 * ms - 1) / (16 * ms)));
+  return stage ? launch_tq1_ms<true>(ms, a, stream, grid, W, lds, RG, WK, nuw, xregion)
+               : launch_tq1_ms<false>(ms, a, stream, grid, W, lds, RG, WK, nuw, xregion);
 }
 
 }  // namespace tq
