@@ -14,6 +14,17 @@ import os
 
 import numpy as np
 
+# One HIP runtime per process.  libtq.so needs libamdhip64.so.7, and the torch
+# wheel carries its own copy of that library (and of the HSA runtime).  If
+# libtq.so were loaded first, the system copy would be mapped and torch would
+# then map its own: two runtimes claiming one GPU, which crashes on the first
+# device allocation.  Importing torch first lets the loader resolve libtq.so's
+# dependency to the copy torch already mapped.
+try:
+    import torch as _torch  # noqa: F401
+except ImportError:  # host-only use without torch: the system runtime is the only one
+    _torch = None
+
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is missing; build it with "

@@ -123,3 +123,18 @@ def test_package_fails_loudly_without_library(tmp_path):
             "try:\n    b.tq_gemm_tq2\nexcept ImportError as e:\n    print('IMPORT-ERROR', e)\n")
     out = subprocess.run(["python", "-c", code], cwd=tmp_path, capture_output=True, text=True)
     assert "IMPORT-ERROR" in out.stdout, out.stdout + out.stderr
+
+
+def test_one_hip_runtime_per_process():
+    """Importing the binding before torch must not map a second HIP runtime:
+    libtq.so and the torch wheel both need libamdhip64.so.7, and two copies in
+    one process crash on the first device allocation."""
+    pytest.importorskip("torch")
+    code = ("import bit_mixed_precision_amd.binding\nimport torch\n"
+            "paths = {l.split()[-1] for l in open('/proc/self/maps')\n"
+            "         if 'libamdhip64' in l or 'libhsa-runtime64' in l}\n"
+            "print(len([p for p in paths if 'amdhip64' in p]),"
+            " len([p for p in paths if 'hsa-runtime64' in p]))\n")
+    out = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True,
+                         check=True).stdout.split()
+    assert out == ["1", "1"], out
