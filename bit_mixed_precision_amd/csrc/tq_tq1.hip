@@ -55,63 +55,68 @@ constexpr int kSpanBytes = 4 * kUnitBytes;  // one 32-byte span of weights, 160 
 // i.e. weight 40 g + 5 kByteOfSlot[s] + j of the span.
 __device__ constexpr int kByteOfSlot[8] = {0, 2, 1, 3, 4, 6, 5, 7};
 
-// Stages the activations of spans [u0, u0 + nu) for rows m_base .. m_base + mrows - 1
-// into LDS in decoder order: for every (m, span u, group g, operand o) 8 halves.
-// o < 5: plain X at the operand's weights (zero past K); o >= 5: the same
-// masked to the weights at or past the span's block boundary.  A unit (m, u, g)
-// covers the 40 consecutive activations k0 = 160 u + 40 g .. k0 + 39: five
-// coalesced 16-byte loads (K and k0 are multiples of 8, so a chunk is either
-// wholly inside the row or wholly past K), then every operand dword is one
-// v_perm_b32 of two loaded dwords.
-__device__ void tq1_stage_x(unsigned char* xs, const uint16_t* __restrict__ X, int mrows,
-                            int m_base, int K, int u0, int nu, int xstride) {
-  const int units = mrows * nu * 4;
-  for (int q = threadIdx.x; q < units; q += blockDim.x) {
-    const int g = q & 3;
-    const int u = (q >> 2) % nu;
-    const int m = (q >> 2) / nu;
-    const int k0 = 160 * (u0 + u) + 40 * g;
-    const int kb = ((160 * (u0 + u)) / 256 + 1) * 256;  // first block boundary of the span
-    const uint16_t* xrow = X + (size_t)(m_base + m) * K;
-    uint32_t e[20];  // activations k0 .. k0 + 39, two per dword
+// Activations in LDS, decoder order: for every (row m, span u, lane group g,
+// operand o) 8 halves.  o < 5: plain X at the operand's weights (zero past K);
+// o >= 5: the same masked to the weights at or past the span's block boundary.
+// A window holds spans [u0, u0 + nu) of rows m_base .. m_base + mrows - 1;
+// thread q stages unit q = (m, u, g) of every window (units <= threads): the
+// 40 consecutive activations k0 = 160 (u0 + u) + 40 g .. k0 + 39, read with
+// five coalesced 16-byte loads (K and k0 are multiples of 8, so a chunk is
+// either wholly inside the row or wholly past K) one window ahead, then
+// written with one v_perm_b32 per operand dword.
+__device__ __forceinline__ void tq1_load_unit(uint32_t (&e)[20], const uint16_t* __restrict__ X,
+                                              int m_base, int K, int u0, int nu, int q) {
+  const int g = q & 3;
+  const int u = (q >> 2) % nu;
+  const int m = (q >> 2) / nu;
+  const int k0 = 160 * (u0 + u) + 40 * g;
+  const uint16_t* xrow = X + (size_t)(m_base + m) * K;
 #pragma unroll
-    for (int c = 0; c < 5; ++c) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (k0 + 8 * c + 8 <= K) v = *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * c);
+  for (int c = 0; c < 5; ++c) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k0 + 8 * c + 8 <= K) v = *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * c);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) e[4 * c + t] = v[t];
+    for (int t = 0; t < 4; ++t) e[4 * c + t] = v[t];
+  }
+}
+
+__device__ __forceinline__ void tq1_store_unit(unsigned char* xs, const uint32_t (&e)[20], int u0,
+                                               int nu, int q, int xstride) {
+  const int g = q & 3;
+  const int u = (q >> 2) % nu;
+  const int m = (q >> 2) / nu;
+  const int k0 = 160 * (u0 + u) + 40 * g;
+  const int kb = ((160 * (u0 + u)) / 256 + 1) * 256;  // first block boundary of the span
+  unsigned char* dst = xs + m * xstride + u * kSpanBytes + g * kUnitBytes;
+  // activations below lim (relative to k0) fall before the block boundary
+  const int lim = kb - k0;
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    uint32_t plain[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // slot pair (2t, 2t + 1) holds activations a = 5 byte(2t) + j, b = 5 byte(2t+1) + j
+      const int a = 5 * kByteOfSlot[2 * t] + j;
+      const int b = 5 * kByteOfSlot[2 * t + 1] + j;
+      const uint32_t sel = ((b & 1) ? 0x07060000u : 0x05040000u) | ((a & 1) ? 0x0302u : 0x0100u);
+      plain[t] = perm(e[b >> 1], e[a >> 1], sel);
     }
-    unsigned char* dst = xs + m * xstride + u * kSpanBytes + g * kUnitBytes;
-    // activations below lim (relative to k0) fall before the block boundary
-    const int lim = kb - k0;
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-      uint32_t plain[4];
+    *reinterpret_cast<u32x4*>(dst + 16 * j) = u32x4{plain[0], plain[1], plain[2], plain[3]};
+    u32x4 masked;
+    if (lim <= 0) {
+      masked = u32x4{plain[0], plain[1], plain[2], plain[3]};
+    } else if (lim >= 40) {
+      masked = u32x4{0u, 0u, 0u, 0u};
+    } else {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        // slot pair (2t, 2t + 1) holds activations a = 5 byte(2t) + j, b = 5 byte(2t+1) + j
         const int a = 5 * kByteOfSlot[2 * t] + j;
         const int b = 5 * kByteOfSlot[2 * t + 1] + j;
-        const uint32_t sel = ((b & 1) ? 0x07060000u : 0x05040000u) | ((a & 1) ? 0x0302u : 0x0100u);
-        plain[t] = perm(e[b >> 1], e[a >> 1], sel);
+        const uint32_t keep = (a >= lim ? 0x0000FFFFu : 0u) | (b >= lim ? 0xFFFF0000u : 0u);
+        masked[t] = plain[t] & keep;
       }
-      *reinterpret_cast<u32x4*>(dst + 16 * j) = u32x4{plain[0], plain[1], plain[2], plain[3]};
-      u32x4 masked;
-      if (lim <= 0) {
-        masked = u32x4{plain[0], plain[1], plain[2], plain[3]};
-      } else if (lim >= 40) {
-        masked = u32x4{0u, 0u, 0u, 0u};
-      } else {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int a = 5 * kByteOfSlot[2 * t] + j;
-          const int b = 5 * kByteOfSlot[2 * t + 1] + j;
-          const uint32_t keep = (a >= lim ? 0x0000FFFFu : 0u) | (b >= lim ? 0xFFFF0000u : 0u);
-          masked[t] = plain[t] & keep;
-        }
-      }
-      *reinterpret_cast<u32x4*>(dst + 16 * (5 + j)) = masked;
     }
+    *reinterpret_cast<u32x4*>(dst + 16 * (5 + j)) = masked;
   }
 }
 
@@ -241,6 +246,10 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
       run(std::false_type{});
   };
 
+  // This thread's staging unit, one window ahead (units <= threads).
+  const int q = threadIdx.x;
+  uint32_t xe[20];
+  if (q < mrows * min(nuw, nu) * 4) tq1_load_unit(xe, X, m_base, K, 0, min(nuw, nu), q);
   for (int u0 = 0; u0 < nu; u0 += nuw) {
     const int nuw_here = min(nuw, nu - u0);
     const int cnt = nuw_here > wk ? (nuw_here - wk + WK - 1) / WK : 0;
@@ -248,8 +257,11 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     if (cnt > 0) {
       sfor1<0, D>([&](auto dd) { load(decltype(dd)::value, span(decltype(dd)::value)); });
     }
-    __syncthreads();
-    tq1_stage_x(smem, X, mrows, m_base, K, u0, nuw_here, xstride);
+    __syncthreads();  // the previous window is consumed
+    if (q < mrows * nuw_here * 4) tq1_store_unit(smem, xe, u0, nuw_here, q, xstride);
+    const int u1 = u0 + nuw;  // the next window's activations fly during this one
+    if (u1 < nu && q < mrows * min(nuw, nu - u1) * 4)
+      tq1_load_unit(xe, X, m_base, K, u1, min(nuw, nu - u1), q);
     __syncthreads();
     for (int i = 0; i < cnt; i += D) {
       sfor1<0, D>([&](auto dd) {
@@ -341,7 +353,8 @@ hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream) {
   const int mrows = M < 16 * ms ? M : 16 * ms;
   int nuw = (kXLds / mrows - kPad) / kSpanBytes;
   if (nuw > nu) nuw = nu;
-  if (nuw < 1) nuw = 1;
+  if (nuw > 64 * W / (4 * mrows)) nuw = 64 * W / (4 * mrows);  // one staging unit per thread
+  if (nuw < 1) return hipErrorInvalidValue;
   const int xbytes = mrows * (nuw * kSpanBytes + kPad);
   const int rbytes = ms * W * 1024;  // the partial sums reuse the window
   int xregion = xbytes > rbytes ? xbytes : rbytes;
