@@ -184,7 +184,7 @@ int tq_gemm_tq2_tiled(const void* X, const void* qs, const void* scales, void* Y
   bool noop = false;
   int st = check_gemm(X, qs, scales, Y, M, N, K, false, 0, &noop);
   if (st != TQ_OK || noop) return st;
-  const tq::TiledShape t{mt, 4, ng, kg};
+  const tq::TiledShape t{mt, mt == 8 ? 2 : 4, ng, kg};
   if (!tq::tiled_compiled(t)) return TQ_ERR_UNSUPPORTED;
   st = device_ready();
   if (st != TQ_OK) return st;

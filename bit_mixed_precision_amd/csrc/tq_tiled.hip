@@ -155,7 +155,7 @@ struct TileGeom {
   static constexpr int kLoop = kSOff + WD * WV * 256;
   static constexpr int kRed = (KG - 1) * NG * MT * NR * 256 * 4;
   static constexpr int kLds = kLoop > kRed ? kLoop : kRed;
-  static_assert(NR == 4, "one scale DMA covers the 64 weight rows of a wave");
+  static_assert(NR <= 4, "one scale DMA (64 lanes) covers the weight rows of a wave");
 };
 
 // Workgroup L runs tile (n_tile, m_tile) with n_tile = 8 (L / 8 / m_tiles) +
@@ -442,7 +442,8 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
 // number of stages a workgroup runs (fewer with more k-groups) and how many
 // compute units have one.  The 8-wave tiles (one workgroup per compute unit,
 // half the activation re-reads) win once they alone fill about 85% of the
-// compute units: 64 x 256 (4 row groups x 2 k-groups) past M = 64, 64 x 128
+// compute units: 128 x 128 (4 row groups of 32 x 2 k-groups: each decoded
+// weight feeds 8 MFMAs, the weights are read once) past M = 64, 64 x 128
 // (2 x 4) up to M = 64.  Below that the 4-wave tile of 1 row group x 4
 // k-groups (BN = 64, twice the workgroups), with 32 activation rows up to
 // M = 64 so that the activation-row tiles spread over more compute units.
@@ -450,9 +451,10 @@ TiledShape tiled_shape(int64_t M, int64_t N) {
   const int64_t cus = device_cus();
   if (M > 32) {
     const bool wide = M > 64;
-    const TiledShape t8 = wide ? TiledShape{4, 4, 4, 2} : TiledShape{4, 4, 2, 4};
-    const int64_t bn = 16 * 4 * t8.ng;
-    const int64_t wgs = ((N + bn - 1) / bn) * ((M + 63) / 64);
+    const TiledShape t8 = wide ? TiledShape{8, 2, 4, 2} : TiledShape{4, 4, 2, 4};
+    const int64_t bm = 16 * t8.mt;
+    const int64_t bn = 16 * t8.nr * t8.ng;
+    const int64_t wgs = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
     if (20 * wgs >= 17 * cus) return t8;
     return wide ? TiledShape{4, 4, 1, 4} : TiledShape{2, 4, 1, 4};
   }
@@ -468,12 +470,14 @@ hipError_t launch_mt(const TiledShape& t, const GemmArgs& a, hipStream_t stream)
 }
 
 bool tiled_compiled(const TiledShape& t) {
+  if (t.mt == 8) return t.nr == 2 && t.ng == 4 && t.kg == 2;
   if ((t.mt != 2 && t.mt != 4) || t.nr != 4) return false;
   return (t.ng == 4 && t.kg == 2) || (t.ng == 2 && t.kg == 4) || (t.ng == 2 && t.kg == 2) ||
          (t.ng == 1 && t.kg == 4);
 }
 
 hipError_t launch_tq2_tiled_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream) {
+  if (t.mt == 8) return launch_tiled<8, 2, 4, 2>(a, stream);
   return t.mt == 2 ? launch_mt<2>(t, a, stream) : launch_mt<4>(t, a, stream);
 }
 

@@ -152,10 +152,11 @@ int tq_gemm_tq1_ex(const void* X, const void* qs, int64_t ldq, const void* scale
                    int64_t M, int64_t N, int64_t K, int path, void* stream);
 
 /* TQ2 product on the tiled kernel with an explicit tile, for tuning and for
- * tests of every tile: 16 mt activation rows x 64 ng weight rows per
- * workgroup of ng x kg waves (kg of them split K).  Compiled tiles: mt in
- * {2, 4} with (ng, kg) in {(4, 2), (2, 4), (2, 2), (1, 4)}; any other tile
- * gives TQ_ERR_UNSUPPORTED.  Everything else is as tq_gemm_tq2. */
+ * tests of every tile: 16 mt activation rows x 64 ng weight rows (32 ng when
+ * mt = 8) per workgroup of ng x kg waves (kg of them split K).  Compiled
+ * tiles: mt in {2, 4} with (ng, kg) in {(4, 2), (2, 4), (2, 2), (1, 4)}, and
+ * mt = 8 with (4, 2); any other tile gives TQ_ERR_UNSUPPORTED.  Everything
+ * else is as tq_gemm_tq2. */
 int tq_gemm_tq2_tiled(const void* X, const void* qs, const void* scales_f16, void* Y,
                       int64_t M, int64_t N, int64_t K, int mt, int ng, int kg, void* stream);
 

@@ -103,6 +103,7 @@ def test_small_parity(fmt, path, M, N, K):
 
 
 TILES = [(mt, ng, kg) for mt in (2, 4) for ng, kg in ((4, 2), (2, 4), (2, 2), (1, 4))]
+TILES.append((8, 4, 2))  # 128 activation rows x 32 weight rows per wave
 # ragged in M and N, K / 256 = 1, 2, 3, 5 (fewer blocks than k-groups, odd counts)
 TILE_SHAPES = [(17, 100, 256), (40, 300, 768), (64, 257, 1024), (100, 520, 1280),
                (130, 1000, 512)]

@@ -17,25 +17,29 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "bit_mixed_precision_amd", "csrc")
 
-# (MT, NG, KG) of the compiled tiles; NR = 4 weight-row groups per wave.
+# (MT, NG, KG) of the compiled tiles; NR(MT) weight-row groups of 16 per wave.
 TILES = [(mt, ng, kg) for mt in (2, 4) for ng, kg in ((4, 2), (2, 4), (2, 2), (1, 4))]
-NR = 4
-W_ISSUE = NR + 1  # weight DMAs plus one scale DMA per round
+TILES.append((8, 4, 2))
+
+
+def nr_of(mt):
+    return 2 if mt == 8 else 4
 
 DRIVER = r"""
 #include <cstdio>
 #include "tq_tiled_sched.h"
 int main() {
-  const int tiles[8][3] = {%s};
+  const int tiles[][4] = {%s};
   for (const auto& t : tiles) {
-    const int mt = t[0], ng = t[1], kg = t[2], wv = ng * kg;
-    const int stage = kg * 16 * mt * 128, round = wv * (%d * 1024 + 256);
+    const int mt = t[0], ng = t[1], kg = t[2], nr = t[3], wv = ng * kg;
+    const int stage = kg * 16 * mt * 128, round = wv * (nr * 1024 + 256);
     const int budget = wv == 8 ? 160 * 1024 : 80 * 1024;
     const tq::RingPlan p = tq::ring_plan(stage, round, budget);
     const int kper = kg * 2 * mt / wv;
     std::printf("%%d %%d %%d %%d %%d %%d", mt, ng, kg, p.xs, p.wd, kper);
     for (int r0 = 1; r0 >= 0; --r0)
-      for (int ch = 0; ch < 4; ++ch) std::printf(" %%d", tq::vm_younger(p.xs, kper, %d, ch, r0));
+      for (int ch = 0; ch < 4; ++ch)
+        std::printf(" %%d", tq::vm_younger(p.xs, kper, nr + 1, ch, r0));
     std::printf("\n");
   }
 }
@@ -49,7 +53,7 @@ def plans(tmp_path_factory):
         pytest.skip("g++ not available")
     d = tmp_path_factory.mktemp("sched")
     src = d / "drv.cpp"
-    src.write_text(DRIVER % (", ".join("{%d, %d, %d}" % t for t in TILES), NR, W_ISSUE))
+    src.write_text(DRIVER % ", ".join("{%d, %d, %d, %d}" % (*t, nr_of(t[0])) for t in TILES))
     exe = d / "drv"
     subprocess.run([gxx, "-std=c++17", "-O1", f"-I{CSRC}", str(src), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
@@ -57,16 +61,18 @@ def plans(tmp_path_factory):
     for line in out.strip().splitlines():
         v = [int(x) for x in line.split()]
         mt, ng, kg, xs, wd, kper = v[:6]
-        rows[(mt, ng, kg)] = dict(xs=xs, wd=wd, kper=kper, r0=v[6:10], rn=v[10:14])
+        rows[(mt, ng, kg)] = dict(xs=xs, wd=wd, kper=kper, r0=v[6:10], rn=v[10:14],
+                                  w_issue=nr_of(mt) + 1)
     assert set(rows) == set(TILES)
     return rows
 
 
-def replay(xs, wd, kper, r0, rn, rounds):
-    """Issue order of one wave; returns the first uncovered read, else None."""
+def replay(xs, wd, kper, r0, rn, rounds, w_issue):
+    """Issue order of one wave; returns the first uncovered read, else None.
+    w_issue: the weight DMAs (one per 16-row group) plus one scale DMA."""
     q = []  # (kind, id)
     for rd in range(wd):
-        q += [("W", rd)] * W_ISSUE
+        q += [("W", rd)] * w_issue
     S = 4 * rounds
     for s in range(xs - 1):
         q += [("X", min(s, S - 1))] * kper
@@ -85,7 +91,7 @@ def replay(xs, wd, kper, r0, rn, rounds):
                 if last_w >= landed:
                     return ("W", rd, ch)
             if ch == 1:
-                q += [("W", rd + wd)] * W_ISSUE
+                q += [("W", rd + wd)] * w_issue
             q += [("X", min(s + xs - 1, S - 1))] * kper
     return None
 
@@ -95,20 +101,22 @@ def test_every_wait_covers_its_data(plans, tile):
     p = plans[tile]
     assert 3 <= p["xs"] <= 6 and p["wd"] in (1, 2) and p["xs"] <= 4 * p["wd"] - 1
     for rounds in (1, 2, 3, 5, 8, 32):
-        assert replay(p["xs"], p["wd"], p["kper"], p["r0"], p["rn"], rounds) is None, (tile, rounds)
+        assert replay(p["xs"], p["wd"], p["kper"], p["r0"], p["rn"], rounds,
+                      p["w_issue"]) is None, (tile, rounds)
 
 
 @pytest.mark.parametrize("tile", TILES)
 def test_ring_fits_lds(plans, tile):
     mt, ng, kg = tile
+    nr = nr_of(mt)
     p, wv = plans[tile], ng * kg
-    ring = p["xs"] * kg * 16 * mt * 128 + p["wd"] * wv * (NR * 1024 + 256)
-    red = (kg - 1) * ng * mt * NR * 256 * 4
+    ring = p["xs"] * kg * 16 * mt * 128 + p["wd"] * wv * (nr * 1024 + 256)
+    red = (kg - 1) * ng * mt * nr * 256 * 4
     budget = 160 * 1024 if wv == 8 else 80 * 1024
     assert max(ring, red) <= 160 * 1024
     if ring <= budget:  # the plan is the deepest candidate that fits
         deeper = [(x, w) for x, w in ((6, 2), (5, 2), (4, 2), (3, 2), (3, 1))
-                  if x * kg * 16 * mt * 128 + w * wv * (NR * 1024 + 256) <= budget]
+                  if x * kg * 16 * mt * 128 + w * wv * (nr * 1024 + 256) <= budget]
         assert (p["xs"], p["wd"]) == deeper[0]
 
 
@@ -123,8 +131,8 @@ def test_a_count_one_too_large_is_caught(plans):
                 bad = dict(p)
                 bad[which] = list(p[which])
                 bad[which][ch] += 1
-                if any(replay(bad["xs"], bad["wd"], bad["kper"], bad["r0"], bad["rn"], r)
-                       for r in (1, 2, 3, 8)):
+                if any(replay(bad["xs"], bad["wd"], bad["kper"], bad["r0"], bad["rn"], r,
+                              p["w_issue"]) for r in (1, 2, 3, 8)):
                     caught += 1
     # every count of every tile is tight
     assert caught == len(TILES) * 8
