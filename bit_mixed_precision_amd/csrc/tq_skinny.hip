@@ -10,10 +10,11 @@
 //    per CU;
 //  * its waves take the 256-weight blocks round robin, so at any time they read
 //    neighbouring 64-byte pieces of the same rows; every lane streams 16-byte
-//    non-temporal loads, double-buffered in registers (only weight loads are in
-//    the vector-memory queue, so the prefetch overlaps the decode);
-//  * the activations of the workgroup are staged once in LDS, already in the
-//    order the decoder produces weights, and the block scales of its rows too;
+//    loads through a ring of register buffers (inside the loop only weight
+//    loads are in the vector-memory queue, so the prefetch overlaps the decode);
+//  * the activations are staged in LDS once per window of K (the whole of K
+//    when it fits) with coalesced loads, scattered into the order the decoder
+//    produces weights; the block scales of the workgroup's rows are staged too;
 //  * trits become fp16 with one v_and_or_b32 against the fp16 exponent of 1024
 //    plus one v_pk_fma_f16 per pair of weights (exact -1 / 0 / +1);
 //  * the multiply-accumulate runs on v_mfma_f32_16x16x32_f16 with the M <= 16
@@ -74,28 +75,40 @@ __device__ __forceinline__ half8 tq2_class(const DecodeConsts& dc, const u32x4& 
 }
 
 // Copies activations of blocks [wb0, wb0 + nbw) of rows m < M into LDS in
-// decoder order (one 64-activation chunk per (m, block, g) per thread step).
+// decoder order.  Consecutive lanes read consecutive 16-byte pieces of a row,
+// so each wave load covers whole cache lines; piece j of a row holds
+// x[64 g + 8 s + c], c = 0..7 (block j / 32, g = j / 8 % 4, s = j % 8), and its
+// eight activations go to their class slots Xt[m][block][g][c][s] with 2-byte
+// LDS writes.  Four pieces per thread are in flight at a time.
 __device__ __forceinline__ void stage_x(unsigned char* xs, const uint16_t* __restrict__ X, int M,
                                         int K, int wb0, int nbw, int xstride) {
-  const int chunks = M * nbw * 4;
-  for (int q = threadIdx.x; q < chunks; q += blockDim.x) {
-    const int g = q & 3;
-    const int bw = (q >> 2) % nbw;
-    const int m = (q >> 2) / nbw;
-    const u32x4* src =
-        reinterpret_cast<const u32x4*>(X + (size_t)m * K + 256 * (wb0 + bw) + 64 * g);
-    u32x4 raw[8];
+  const int per_row = nbw * 32;
+  const int total = M * per_row;
+  const int T = blockDim.x;
+  for (int p0 = threadIdx.x; p0 < total; p0 += 4 * T) {
+    u32x4 v[4];
+    int dst[4];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) raw[s] = src[s];
-    unsigned char* dst = xs + m * xstride + bw * 512 + g * 128;
-    static_for<0, 8>([&](auto cc) {
-      constexpr int c = decltype(cc)::value;
-      constexpr uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 a;
+    for (int u = 0; u < 4; ++u) {
+      int p = p0 + u * T;
+      const bool ok = p < total;
+      p = ok ? p : 0;  // past the end: a valid dummy read, not stored
+      const int m = p / per_row;
+      const int j = p - m * per_row;
+      v[u] = *reinterpret_cast<const u32x4*>(X + (size_t)m * K + 256 * wb0 + 8 * j);
+      dst[u] = ok ? m * xstride + (j >> 5) * 512 + ((j >> 3) & 3) * 128 + (j & 7) * 2 : -1;
+    }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) a[t] = perm(raw[2 * t + 1][c >> 1], raw[2 * t][c >> 1], sel);
-      *reinterpret_cast<u32x4*>(dst + 16 * c) = a;
-    });
+    for (int u = 0; u < 4; ++u) {
+      if (dst[u] >= 0) {
+        unsigned char* d = xs + dst[u];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const uint32_t wv = v[u][c >> 1];
+          *reinterpret_cast<uint16_t*>(d + 16 * c) = (uint16_t)((c & 1) ? (wv >> 16) : wv);
+        }
+      }
+    }
   }
 }
 
@@ -170,13 +183,15 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   for (int wb0 = 0; wb0 < nb; wb0 += nbw) {
     const int nbw_here = min(nbw, nb - wb0);
     const int cnt = nbw_here > wk ? (nbw_here - wk + WK - 1) / WK : 0;
-    // block of step i; past the end, the wave's last real block (a cache hit)
-    auto blk = [&](int i) { return wb0 + wk + WK * (i < cnt ? i : cnt - 1); };
-    if (cnt > 0) {
-      static_for<0, D>([&](auto dd) { load(decltype(dd)::value, blk(decltype(dd)::value)); });
-    }
+    // block of step i; past the end, the wave's last real block (a cache hit);
+    // a wave with no block in the window refetches block wb0
+    auto blk = [&](int i) { return cnt > 0 ? wb0 + wk + WK * (i < cnt ? i : cnt - 1) : wb0; };
     __syncthreads();  // earlier window fully consumed
     stage_x(smem, X, M, K, wb0, nbw_here, xstride);
+    // The first D weight loads go out after the activation loads, so waiting
+    // for those does not wait for these; the prefetch is unconditional, which
+    // keeps the compiler's count of loads in flight exact in the loop below.
+    static_for<0, D>([&](auto dd) { load(decltype(dd)::value, blk(decltype(dd)::value)); });
     __syncthreads();
     for (int i = 0; i < cnt; i += D) {
       static_for<0, D>([&](auto dd) {
