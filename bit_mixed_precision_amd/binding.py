@@ -56,6 +56,7 @@ SIGNATURES = {
     "tq_gemm_tq2_ex": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "tq_gemm_tq1_ex": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _P]),
     "tq_gemm_tq2_tiled": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
+    "tq_gemm_tq1_tiled": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -214,6 +215,16 @@ def tq_gemm_tq2_tiled(X, qs, scales, mt: int, ng: int, kg: int, Y=None, stream=N
     Y = _out(Y, M, N, X)
     _check(lib.tq_gemm_tq2_tiled(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, ng, kg,
                                  _stream(stream)), "tq_gemm_tq2_tiled")
+    return Y
+
+
+def tq_gemm_tq1_tiled(X, qs, scales, mt: int, nw: int, kg: int, Y=None, stream=None):
+    """tq_gemm_tq1 on the tiled kernel with an explicit (mt, nw, kg) tile."""
+    M, K = X.shape
+    N, ldq = qs.shape
+    Y = _out(Y, M, N, X)
+    _check(lib.tq_gemm_tq1_tiled(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K, mt, nw,
+                                 kg, _stream(stream)), "tq_gemm_tq1_tiled")
     return Y
 
 

@@ -57,8 +57,9 @@ struct Choice {
   const char* name;  // kernel template, as profilers list it
   int variant;       // first template argument, or -1 for none
   int variant2;      // second template argument, or -1 for none
-  int variant3 = -1;  // third and fourth template arguments, or -1 for none
+  int variant3 = -1;  // third to fifth template arguments, or -1 for none
   int variant4 = -1;
+  int variant5 = -1;
 };
 
 constexpr int64_t kSkinnyMaxM = 16;
@@ -66,8 +67,10 @@ constexpr int64_t kSkinnyMaxM = 16;
 // The kernel each (format, shape, path) runs.  Shapes are already validated.
 Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
   if (path == TQ_PATH_AUTO) {
-    if (tq1) path = TQ_PATH_SKINNY;
-    else path = M <= kSkinnyMaxM ? TQ_PATH_SKINNY : TQ_PATH_TILED;
+    if (tq1)
+      path = M > kSkinnyMaxM && tq::tq1_prefers_tiled(M, N) ? TQ_PATH_TILED : TQ_PATH_SKINNY;
+    else
+      path = M <= kSkinnyMaxM ? TQ_PATH_SKINNY : TQ_PATH_TILED;
   }
   switch (path) {
     case TQ_PATH_SIMPLE:
@@ -81,7 +84,11 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
       return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_depth(),
                     tq::skinny_stage(N, K)};
     case TQ_PATH_TILED: {
-      if (tq1) return Choice{nullptr, "", -1, -1};
+      if (tq1) {
+        const tq::Tq1TiledShape t = tq::tq1_tiled_shape(M, N);
+        return Choice{tq::launch_tq1_tiled, "tq1_tiled_kernel", t.mt, t.nw, t.kg,
+                      tq::tq1_tiled_depth(), tq::tq1_tiled_xahead(t)};
+      }
       const tq::TiledShape t = tq::tiled_shape(M, N);
       return Choice{tq::launch_tq2_tiled, "tq2_tiled_kernel", t.mt, t.nr, t.ng, t.kg};
     }
@@ -164,6 +171,9 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
              c.variant3);
   else if (c.variant2 >= 0 && c.launch == tq::launch_tq2_skinny)
     snprintf(buf, sizeof buf, "%s<%d, %s>", c.name, c.variant, c.variant2 ? "true" : "false");
+  else if (c.variant5 >= 0)
+    snprintf(buf, sizeof buf, "%s<%d, %d, %d, %d, %d>", c.name, c.variant, c.variant2,
+             c.variant3, c.variant4, c.variant5);
   else if (c.variant4 >= 0)
     snprintf(buf, sizeof buf, "%s<%d, %d, %d, %d>", c.name, c.variant, c.variant2, c.variant3,
              c.variant4);
@@ -190,6 +200,19 @@ int tq_gemm_tq2_tiled(const void* X, const void* qs, const void* scales, void* Y
   if (st != TQ_OK) return st;
   tq::GemmArgs a{X, qs, scales, Y, M, N, K, 0};
   return finish(tq::launch_tq2_tiled_shape(t, a, static_cast<hipStream_t>(stream)));
+}
+
+int tq_gemm_tq1_tiled(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,
+                      int64_t M, int64_t N, int64_t K, int mt, int nw, int kg, void* stream) {
+  bool noop = false;
+  int st = check_gemm(X, qs, scales, Y, M, N, K, true, ldq, &noop);
+  if (st != TQ_OK || noop) return st;
+  const tq::Tq1TiledShape t{mt, nw, kg};
+  if (!tq::tq1_tiled_compiled(t)) return TQ_ERR_UNSUPPORTED;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  tq::GemmArgs a{X, qs, scales, Y, M, N, K, ldq};
+  return finish(tq::launch_tq1_tiled_shape(t, a, static_cast<hipStream_t>(stream)));
 }
 
 int tq_gemm_tq2(const void* X, const void* qs, const void* scales, void* Y, int64_t M, int64_t N,

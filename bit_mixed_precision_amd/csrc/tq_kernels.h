@@ -46,4 +46,17 @@ bool tiled_compiled(const TiledShape& t);  // one of the instantiated tiles
 hipError_t launch_tq2_tiled(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_tq2_tiled_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream);
 
+// Tiled MFMA kernel for TQ1 and M > 16: a workgroup of nw x kg waves (kg of
+// them split K) owns 16 mt activation rows x 16 nw weight rows.
+struct Tq1TiledShape {
+  int mt, nw, kg;
+};
+Tq1TiledShape tq1_tiled_shape(int64_t M, int64_t N);
+bool tq1_prefers_tiled(int64_t M, int64_t N);  // the automatic choice for M > 16
+bool tq1_tiled_compiled(const Tq1TiledShape& t);
+int tq1_tiled_depth();                           // weight ring depth in stages
+int tq1_tiled_xahead(const Tq1TiledShape& t);    // stages the activations are loaded ahead
+hipError_t launch_tq1_tiled(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_tq1_tiled_shape(const Tq1TiledShape& t, const GemmArgs& a, hipStream_t stream);
+
 }  // namespace tq

@@ -31,6 +31,7 @@
 #include "tq_common.h"
 #include "tq_kernels.h"
 #include "tq_mfma.h"
+#include "tq_tq1.h"
 
 namespace tq {
 namespace {
@@ -47,14 +48,6 @@ constexpr int kPad = 16;
 constexpr int kXLds = 128 * 1024;   // activation window budget
 constexpr int kScLds = 24 * 1024;   // staged scales budget
 constexpr int kLdsMax = 160 * 1024;
-// Per (row m, span u, lane group g): 10 operands of 16 bytes (5 plain, 5 masked).
-constexpr int kUnitBytes = 10 * 16;
-constexpr int kSpanBytes = 4 * kUnitBytes;  // one 32-byte span of weights, 160 weights
-
-// Slot s of operand j holds byte kByteOfSlot[s] of the lane's 8 bytes, digit j,
-// i.e. weight 40 g + 5 kByteOfSlot[s] + j of the span.
-__device__ constexpr int kByteOfSlot[8] = {0, 2, 1, 3, 4, 6, 5, 7};
-
 // Activations in LDS, decoder order: for every (row m, span u, lane group g,
 // operand o) 8 halves.  o < 5: plain X at the operand's weights (zero past K);
 // o >= 5: the same masked to the weights at or past the span's block boundary.
@@ -87,58 +80,8 @@ __device__ __forceinline__ void tq1_store_unit(unsigned char* xs, const uint32_t
   const int m = (q >> 2) / nu;
   const int k0 = 160 * (u0 + u) + 40 * g;
   const int kb = ((160 * (u0 + u)) / 256 + 1) * 256;  // first block boundary of the span
-  unsigned char* dst = xs + m * xstride + u * kSpanBytes + g * kUnitBytes;
-  // activations below lim (relative to k0) fall before the block boundary
-  const int lim = kb - k0;
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    uint32_t plain[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      // slot pair (2t, 2t + 1) holds activations a = 5 byte(2t) + j, b = 5 byte(2t+1) + j
-      const int a = 5 * kByteOfSlot[2 * t] + j;
-      const int b = 5 * kByteOfSlot[2 * t + 1] + j;
-      const uint32_t sel = ((b & 1) ? 0x07060000u : 0x05040000u) | ((a & 1) ? 0x0302u : 0x0100u);
-      plain[t] = perm(e[b >> 1], e[a >> 1], sel);
-    }
-    *reinterpret_cast<u32x4*>(dst + 16 * j) = u32x4{plain[0], plain[1], plain[2], plain[3]};
-    u32x4 masked;
-    if (lim <= 0) {
-      masked = u32x4{plain[0], plain[1], plain[2], plain[3]};
-    } else if (lim >= 40) {
-      masked = u32x4{0u, 0u, 0u, 0u};
-    } else {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int a = 5 * kByteOfSlot[2 * t] + j;
-        const int b = 5 * kByteOfSlot[2 * t + 1] + j;
-        const uint32_t keep = (a >= lim ? 0x0000FFFFu : 0u) | (b >= lim ? 0xFFFF0000u : 0u);
-        masked[t] = plain[t] & keep;
-      }
-    }
-    *reinterpret_cast<u32x4*>(dst + 16 * (5 + j)) = masked;
-  }
+  tq1_store_operands(xs + m * xstride + u * kSpanBytes + g * kUnitBytes, e, kb - k0);
 }
-
-// Five digit steps of the multiply decoder on two bytes (one per 16-bit half).
-struct Tq1Decoder {
-  uint32_t magic, mul, add;
-  __device__ __forceinline__ void init() {
-    magic = in_vgpr(kMagic2);
-    mul = in_vgpr(pack_half2(1.0f / 256.0f, 1.0f / 256.0f));
-    add = in_vgpr(pack_half2(-5.0f, -5.0f));
-  }
-  // t = 3 q; returns the fp16 trit pair (digit - 1) of t's high byte; q <- t & 0xff.
-  __device__ __forceinline__ uint32_t step(uint32_t& q) const {
-    const uint32_t t = (q << 1) + q;  // no carry between halves: 3 * 255 < 2^16
-    const uint32_t v = (t & 0x03000300u) | magic;  // 1024 + 256 * digit
-    q = t & 0x00FF00FFu;
-    const half2v d = __builtin_elementwise_fma(__builtin_bit_cast(half2v, v),
-                                               __builtin_bit_cast(half2v, mul),
-                                               __builtin_bit_cast(half2v, add));
-    return __builtin_bit_cast(uint32_t, d);
-  }
-};
 
 template <int D, bool STAGE, int MS>
 __global__ __launch_bounds__(1024) void tq1_skinny_kernel(

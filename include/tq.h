@@ -57,9 +57,11 @@ typedef enum {
   TQ_SRC_LATENT_F32 = 1  /* float [N][K] latent weights, ternarized with eps        */
 } tq_src;
 
-/* Kernel family for tq_gemm_*_ex.  AUTO picks the skinny kernel for M <= 16 and
- * the tiled MFMA kernel above; the others force one family at any M (used by
- * the tests to cover both sides of the switch). */
+/* Kernel family for tq_gemm_*_ex.  AUTO picks, for TQ2, the skinny kernel for
+ * M <= 16 and the tiled MFMA kernel above; for TQ1, the tiled kernel for
+ * M >= 48 with N <= 16384 and the skinny kernel otherwise (measured at
+ * K = 8192).  The others force one family at any M (used by the tests to
+ * cover both sides of the switch). */
 typedef enum {
   TQ_PATH_AUTO = 0,
   TQ_PATH_SKINNY = 1,
@@ -159,6 +161,14 @@ int tq_gemm_tq1_ex(const void* X, const void* qs, int64_t ldq, const void* scale
  * else is as tq_gemm_tq2. */
 int tq_gemm_tq2_tiled(const void* X, const void* qs, const void* scales_f16, void* Y,
                       int64_t M, int64_t N, int64_t K, int mt, int ng, int kg, void* stream);
+
+/* TQ1 product on the tiled kernel with an explicit tile, for tuning and for
+ * tests of every tile: 16 mt activation rows x 16 nw weight rows per
+ * workgroup of nw x kg waves (kg of them split K).  Compiled tiles: (mt, nw,
+ * kg) in {(1, 4, 4), (2, 4, 2), (2, 4, 4), (4, 4, 1), (4, 4, 2), (2, 8, 2)};
+ * any other gives TQ_ERR_UNSUPPORTED.  Everything else is as tq_gemm_tq1. */
+int tq_gemm_tq1_tiled(const void* X, const void* qs, int64_t ldq, const void* scales_f16, void* Y,
+                      int64_t M, int64_t N, int64_t K, int mt, int nw, int kg, void* stream);
 
 #ifdef __cplusplus
 }

@@ -91,6 +91,20 @@ def test_tiled_tile_errors():
     assert _gt(3, 2, 2, X=None, M=0) == tq.TQ_OK
 
 
+def _gt1(mt, nw, kg, X=A, M=40, K=512, ldq=112):
+    return tq.raw_call("tq_gemm_tq1_tiled", X, A, ldq, A, A, M, 64, K, mt, nw, kg, None)
+
+
+def test_tq1_tiled_tile_errors():
+    assert _gt1(2, 4, 4, X=None) == tq.TQ_ERR_NULL
+    assert _gt1(2, 4, 4, K=300) == tq.TQ_ERR_SHAPE
+    assert _gt1(2, 4, 4, ldq=96) == tq.TQ_ERR_SHAPE  # < ceil(512/5)
+    for tile in [(3, 4, 4), (8, 4, 1), (1, 8, 2), (2, 8, 4), (4, 2, 2), (0, 4, 4), (2, 4, 3),
+                 (2, 4, 1)]:
+        assert _gt1(*tile) == tq.TQ_ERR_UNSUPPORTED, tile
+    assert _gt1(3, 4, 4, X=None, M=0) == tq.TQ_OK
+
+
 @pytest.mark.skipif(HAS_GPU, reason="checks the no-device error; a GPU is present")
 def test_gemm_without_device():
     assert _g2() == tq.TQ_ERR_DEVICE

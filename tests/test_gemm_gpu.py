@@ -124,6 +124,28 @@ def test_every_tiled_tile(mt, ng, kg, M, N, K):
     check_close(Y.cpu().numpy(), ref(X, T, s), f"tile {mt},{ng},{kg} {M}x{N}x{K}")
 
 
+TQ1_TILES = [(1, 4, 4), (2, 4, 2), (2, 4, 4), (4, 4, 1), (4, 4, 2), (2, 8, 2)]
+# ragged in M and N; K with 1, 3, 4, 5 blocks: spans with and without a block
+# boundary, a last span past ldq, ldq larger than ceil(K / 5)
+TQ1_TILE_SHAPES = [(17, 100, 256, None), (40, 300, 768, None), (64, 257, 1024, 224),
+                   (100, 130, 1280, None), (130, 70, 512, 128)]
+
+
+@pytest.mark.parametrize("mt,nw,kg", TQ1_TILES)
+@pytest.mark.parametrize("M,N,K,ldq", TQ1_TILE_SHAPES)
+def test_every_tq1_tiled_tile(mt, nw, kg, M, N, K, ldq):
+    say(f"[tq1 tile] mt={mt} nw={nw} kg={kg} M={M} N={N} K={K} ldq={ldq}")
+    T, s = iid_problem(N, K, 0.31, 6)
+    X = activations(M, K, 6)
+    ldq = ldq or tq.tq_tq1_ldq(K)
+    q = tq.tq_pack_tq1(T, ldq=ldq)[0]
+    Xd, qd, sd = dev(X), dev(q), dev(s)
+    Y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    tq.tq_gemm_tq1_tiled(Xd, qd, sd, mt, nw, kg, Y)
+    torch.cuda.synchronize()
+    check_close(Y.cpu().numpy(), ref(X, T, s), f"tq1 tile {mt},{nw},{kg} {M}x{N}x{K} ldq={ldq}")
+
+
 @pytest.mark.parametrize("path", ["simple", "skinny", "tiled"])
 @pytest.mark.parametrize("fmt", ["tq2", "tq1"])
 def test_exact_special_cases(fmt, path):
