@@ -64,6 +64,14 @@ def workload_calls():
     return calls
 
 
+PREFILL_MS = [256, 1024, 4096]
+
+
+def prefill_calls():
+    """Prompt-sized products on the same two shapes (both formats)."""
+    return [(fmt, M, N, K) for fmt in ("tq2", "tq1") for K, N in SHAPES for M in PREFILL_MS]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -112,7 +120,7 @@ def run_call(tq, fmt, M, N, K, rings, xs, ys, stream):
         raise RuntimeError(f"tq_gemm_{fmt} failed: {tq.tq_status_string(st)}")
 
 
-def gpu_bench(args):
+def gpu_bench(args, calls):
     """Time the step through HIP graphs (one captured graph per timed step, the
     calls inside rotate through the buffer rings), so host launch overhead is
     not in the measurement.  Per-call averages come from one graph per call
@@ -122,7 +130,6 @@ def gpu_bench(args):
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     torch.cuda.set_device(0)
-    calls = workload_calls()
     rings, xs, ys = build_inputs(torch, tq, calls)
     torch.cuda.synchronize()
 
@@ -294,15 +301,43 @@ def main():
     ap.add_argument("--reps", type=int, default=30, help="launches per call when timing each call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calls-out", default=None, help="also write the per-call table here (JSON)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="prompt-sized products (M = 256 .. 4096) instead of the M <= 128 step")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the product has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
-    calls, per_call, ms_step = gpu_bench(args)
+    calls = prefill_calls() if args.prefill else workload_calls()
+    if args.prefill:
+        args.reps = min(args.reps, 3)
+    calls, per_call, ms_step = gpu_bench(args, calls)
     roof_sum = sum(t_roof(*c) for c in calls)
     value = roof_sum / (ms_step * 1e-3)
+    if args.prefill:
+        out = {
+            "metric": "ternary GEMM TFLOP/s vs FP16 MFMA peak at prefill sizes M=256..4096, K=8192 "
+                      "(TQ2, TQ1)",
+            "value": round(value, 4),
+            "unit": "fraction of roofline (FP16 MFMA 2.5 PFLOP/s; every call is MFMA-bound)",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "TQ2 and TQ1, M in {256, 1024, 4096} on (K,N)=(8192,8192),"
+                                   "(8192,28672); i.i.d. trits, fp16 block scales",
+                       "global_batch": None, "seq_len": None, "parallelism": "none"},
+            "roofline": roofline_of(per_call),
+            "tflops_total": round(sum(alg_flops(*c[1:]) for c in calls) / (ms_step * 1e-3) / 1e12,
+                                  1),
+        }
+        if not args.no_cpu_baseline:
+            log("[bench] CPU baseline (oracle) ...")
+            out["cpu_baseline"] = cpu_baseline(calls, cols=64)
+        out["calls"] = per_call
+        print(json.dumps(out), flush=True)
+        return
     out = {
         "metric": "ternary GEMM TB/s + TFLOP/s vs roofline at M=1..128, K=8192 (TQ2, TQ1)",
         "value": round(value, 4),

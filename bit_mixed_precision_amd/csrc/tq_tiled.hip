@@ -158,21 +158,27 @@ struct TileGeom {
   static_assert(NR <= 4, "one scale DMA (64 lanes) covers the weight rows of a wave");
 };
 
-// Workgroup L runs tile (n_tile, m_tile) with n_tile = 8 (L / 8 / m_tiles) +
-// L % 8 and m_tile = (L / 8) % m_tiles: consecutive workgroups go to
-// different XCDs, and the m tiles of one weight-row tile run back to back on
-// the same XCD, so its weights are read from HBM once.
+// Workgroup L runs on XCD L % 8; j = L / 8 orders the tiles an XCD runs.
+// n-major (m_outer = 0): n_tile = 8 (j / m_tiles) + L % 8, m_tile = j % m_tiles:
+// the m tiles of one weight-row tile run back to back on one XCD, so its
+// weights are read from HBM once.  m-major (m_outer = 1, for many m tiles):
+// m_tile = j / groups, n_tile = 8 (j % groups) + L % 8 with groups =
+// ceil(n_tiles / 8): an XCD walks its weight tiles under one activation tile,
+// which stays in its L2, instead of streaming all of X once per weight tile.
 template <int MT, int NR, int NG, int KG>
 __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(const uint16_t* __restrict__ X,
                                                         const uint8_t* __restrict__ qs,
                                                         const uint16_t* __restrict__ scales,
                                                         uint16_t* __restrict__ Y, int M, int N,
-                                                        int K, int n_tiles, int m_tiles) {
+                                                        int K, int n_tiles, int m_tiles,
+                                                        int m_outer) {
   using G = TileGeom<MT, NR, NG, KG>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int L = blockIdx.x;
-  const int m_tile = (L >> 3) % m_tiles;
-  const int n_tile = ((L >> 3) / m_tiles) * 8 + (L & 7);
+  const int j = L >> 3;
+  const int groups = (n_tiles + 7) >> 3;
+  const int m_tile = m_outer ? j / groups : j % m_tiles;
+  const int n_tile = (m_outer ? j % groups : j / m_tiles) * 8 + (L & 7);
   if (n_tile >= n_tiles) return;  // whole workgroup
   const int n_base = n_tile * G::BN;
   const int m_base = m_tile * G::BM;
@@ -410,6 +416,9 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
   }
 }
 
+// From this many activation tiles on, the m-major order (see the kernel).
+constexpr int64_t kMOuterTiles = 4;
+
 template <int MT, int NR, int NG, int KG>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
   using G = TileGeom<MT, NR, NG, KG>;
@@ -431,7 +440,7 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
                      stream, static_cast<const uint16_t*>(a.X),
                      static_cast<const uint8_t*>(a.qs), static_cast<const uint16_t*>(a.scales),
                      static_cast<uint16_t*>(a.Y), (int)a.M, (int)a.N, (int)a.K, (int)n_tiles,
-                     (int)m_tiles);
+                     (int)m_tiles, m_tiles >= kMOuterTiles ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -278,6 +278,26 @@ def test_full_size_tq1(N, p):
         check_close(Y[:, cols], ref(X, T, s, cols=cols), f"full tq1 N={N} p={p} M={M}")
 
 
+PREFILL = [(256, 8192), (1024, 8192), (4096, 8192), (256, 28672)]
+
+
+@pytest.mark.parametrize("fmt", ["tq2", "tq1"])
+@pytest.mark.parametrize("M,N", PREFILL)
+def test_prefill_sizes(fmt, M, N):
+    """Prompt-sized products (K = 8192) on the automatic kernel choice: 64
+    sampled columns against the oracle, all outputs finite."""
+    K = 8192
+    T, s = iid_problem(N, K, 0.31, 70)
+    q = pack(fmt, T)
+    cols = np.sort(seed_for(71, N).choice(N, 64, replace=False))
+    cols[0], cols[-1] = 0, N - 1
+    say(f"[prefill] {fmt} M={M} N={N} kernel={tq.tq_kernel_name(2 if fmt == 'tq2' else 1, M, N, K)}")
+    X = activations(M, K, 70 + M)
+    Y = run(fmt, X, q, s, "auto").cpu().numpy()
+    assert np.all(np.isfinite(Y.astype(np.float32)))
+    check_close(Y[:, cols], ref(X, T, s, cols=cols), f"prefill {fmt} M={M} N={N}")
+
+
 def test_empty_is_noop():
     X = torch.empty((0, 256), dtype=torch.float16, device="cuda")
     q = torch.empty((16, 64), dtype=torch.uint8, device="cuda")
