@@ -291,6 +291,69 @@ def cpu_baseline(calls, cols=1024):
             "TFLOPps": round(total_flops / total_t / 1e12, 6)}
 
 
+# ----------------------------------------------------------------------------- device pack
+
+PACK_SHAPE = (28672, 8192)  # (N, K): the largest linear of the sweep, 940 MB of fp32 latents
+
+
+def pack_bytes(fmt, N, K):
+    """The method's traffic: gamma needs all of |W| before any trit is known, so
+    W is read twice (4 B per weight each), then qs and the scales are written."""
+    q = N * K // 4 if fmt == 2 else N * tq1_ldq(K)
+    return 2 * 4 * N * K + q + 2 * N * (K // 256)
+
+
+def pack_bench(args):
+    import torch
+    import bit_mixed_precision_amd.binding as tq
+    from synth import latent_weights_f32, seed_for
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    torch.cuda.set_device(0)
+    N, K = PACK_SHAPE
+    W = torch.from_numpy(latent_weights_f32(seed_for(700, N, K), N, K)).cuda()
+    stream = torch.cuda.current_stream()
+    out = []
+    for fmt in (2, 1):
+        tq.tq_pack_dev(fmt, W)  # warm
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            _, _, _, st = tq.tq_pack_dev(fmt, W)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        assert int(st.item()) == tq.TQ_OK
+        us = e0.elapsed_time(e1) / reps * 1e3
+        b = pack_bytes(fmt, N, K)
+        out.append({"fmt": "tq%d" % fmt, "N": N, "K": K, "us": round(us, 1),
+                    "TBps": round(b / us / 1e6, 3), "hbm_frac": round(b / HBM_PEAK / (us * 1e-6), 4)})
+        log(f"[bench] pack tq{fmt}: {us:.1f} us, {b / us / 1e6:.2f} TB/s")
+    return out
+
+
+def pack_cpu_baseline(rows=64):
+    """The oracle's ternarize + pack on ``rows`` rows of the same latents
+    (gamma over those rows), time scaled by N / rows."""
+    from oracle import pack_tq1_ref, pack_tq2_ref, ternarize_ref
+    from synth import latent_weights_f32, seed_for
+    N, K = PACK_SHAPE
+    W = latent_weights_f32(seed_for(701, rows, K), rows, K)
+    res = {}
+    for fmt in (2, 1):
+        t = time.perf_counter()
+        T, _ = ternarize_ref(W, 1e-5)
+        pack_tq2_ref(T) if fmt == 2 else pack_tq1_ref(T)
+        res["tq%d" % fmt] = (time.perf_counter() - t) * (N / rows)
+    tot_b = sum(pack_bytes(f, N, K) for f in (2, 1))
+    tot_t = sum(res.values())
+    return {"value": round(tot_b / tot_t / 1e12 / (HBM_PEAK / 1e12), 8),
+            "unit": "fraction of HBM roofline", "cores": 1, "kind": "oracle",
+            "sample": f"ternarize + pack of {rows} rows of the {N} x {K} latents, time scaled "
+                      f"by N/{rows}", "s_tq2": round(res["tq2"], 3), "s_tq1": round(res["tq1"], 3)}
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -301,6 +364,8 @@ def main():
     ap.add_argument("--reps", type=int, default=30, help="launches per call when timing each call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calls-out", default=None, help="also write the per-call table here (JSON)")
+    ap.add_argument("--pack", action="store_true",
+                    help="on-device ternarize + pack of a 28672 x 8192 latent matrix")
     ap.add_argument("--prefill", action="store_true",
                     help="prompt-sized products (M = 256 .. 4096) instead of the M <= 128 step")
     args = ap.parse_args()
@@ -309,6 +374,31 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    if args.pack:
+        rows = pack_bench(args)
+        t_roof_sum = sum(pack_bytes(2 if r["fmt"] == "tq2" else 1, r["N"], r["K"]) for r in rows)
+        t_sum = sum(r["us"] for r in rows) * 1e-6
+        best = max(rows, key=lambda r: r["us"])
+        out = {
+            "metric": "on-device ternarize + pack throughput vs HBM roofline (TQ2, TQ1)",
+            "value": round(t_roof_sum / HBM_PEAK / t_sum, 4),
+            "unit": "fraction of HBM roofline (8 TB/s); W is read twice, qs and scales written",
+            "n_gpus": 1, "steps": args.steps, "warmup": 1, "ms_per_step": round(t_sum * 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "latents N(0, 0.02) fp32, N x K = %d x %d, eps = 1e-5"
+                                   % PACK_SHAPE, "global_batch": None, "seq_len": None,
+                       "parallelism": "none"},
+            "roofline": {"kernel": "tq_pack_tq%s_dev (3 kernels)" % best["fmt"][-1],
+                         "bound": "hbm", "achieved": round(best["TBps"] * 1e3, 1),
+                         "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": best["hbm_frac"],
+                         "traffic": None},
+            "calls": rows,
+        }
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = pack_cpu_baseline()
+        print(json.dumps(out), flush=True)
+        return
     calls = prefill_calls() if args.prefill else workload_calls()
     if args.prefill:
         args.reps = min(args.reps, 3)

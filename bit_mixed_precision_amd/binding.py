@@ -57,6 +57,9 @@ SIGNATURES = {
     "tq_gemm_tq1_ex": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _P]),
     "tq_gemm_tq2_tiled": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_gemm_tq1_tiled": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
+    "tq_pack_dev_workspace_bytes": (_I64, [_I64, _I64]),
+    "tq_pack_tq2_dev": (_I, [_P, _I64, _I64, C.c_double, _P, _P, _P, _P, _P, _I64, _P]),
+    "tq_pack_tq1_dev": (_I, [_P, _I64, _I64, C.c_double, _I64, _P, _P, _P, _P, _P, _I64, _P]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -226,6 +229,34 @@ def tq_gemm_tq1_tiled(X, qs, scales, mt: int, nw: int, kg: int, Y=None, stream=N
     _check(lib.tq_gemm_tq1_tiled(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K, mt, nw,
                                  kg, _stream(stream)), "tq_gemm_tq1_tiled")
     return Y
+
+
+def tq_pack_dev(fmt: int, W, eps: float = 1e-5, ldq: int | None = None, stream=None):
+    """On-device ternarize + pack of a float32 [N][K] device tensor W (fmt 2 or 1).
+    Returns device tensors (qs, scales fp16, gamma fp64 [1], status int32 [1])."""
+    import torch
+    N, K = W.shape
+    dev = W.device
+    if fmt == 2:
+        qs = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
+    else:
+        ldq = tq_tq1_ldq(K) if ldq is None else ldq
+        qs = torch.empty((N, max(ldq, 0)), dtype=torch.uint8, device=dev)
+    scales = torch.empty((N, K // 256), dtype=torch.float16, device=dev)
+    gamma = torch.empty(1, dtype=torch.float64, device=dev)
+    status = torch.empty(1, dtype=torch.int32, device=dev)
+    wsb = lib.tq_pack_dev_workspace_bytes(N, K)
+    if wsb < 0:
+        raise TQError(TQ_ERR_SHAPE, "tq_pack_dev_workspace_bytes")
+    ws = torch.empty(int(wsb), dtype=torch.uint8, device=dev)
+    if fmt == 2:
+        st = lib.tq_pack_tq2_dev(_ptr(W), N, K, float(eps), _ptr(qs), _ptr(scales), _ptr(gamma),
+                                 _ptr(status), _ptr(ws), wsb, _stream(stream))
+    else:
+        st = lib.tq_pack_tq1_dev(_ptr(W), N, K, float(eps), ldq, _ptr(qs), _ptr(scales),
+                                 _ptr(gamma), _ptr(status), _ptr(ws), wsb, _stream(stream))
+    _check(st, "tq_pack_tq%d_dev" % fmt)
+    return qs, scales, gamma, status
 
 
 def tq_gemm_tq2(X, qs, scales, Y=None, stream=None):

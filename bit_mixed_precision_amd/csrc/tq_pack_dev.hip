@@ -1,0 +1,364 @@
+// On-device ternarization and packing (the step before the product):
+// gamma = eps + mean|W| over the whole matrix, T = round(clip(W / gamma, -1, 1)),
+// then the TQ2 or TQ1 packing with fp16(gamma) in every block scale.
+//
+// Follows the project page "Scaling Laws and Efficient Inference for Ternary
+// Language Models": "The model" (steps 1-2) for the ternarization, "Packing
+// ternary weights" for both packings, "Fast inference on CPUs" for the
+// 256-weight scale block.  The results are the host packer's bit for bit: the
+// sum of |W| is exact (integer sums per fp32 exponent, rounded once to fp64),
+// the quotient W / gamma is the same correctly rounded fp64 division, and the
+// ties of round() go to even (only |q| > 1/2 leaves zero).
+//
+// Four kernels on one stream, no host round trip:
+//  * tq_abs_sum_kernel: every workgroup adds the 24-bit significands of its
+//    elements into 256 per-exponent 64-bit buckets in LDS, then adds each
+//    bucket into a 128-bit total in the workspace (64-bit integer atomics, the
+//    carry counted in the high word); integer sums do not depend on the order,
+//    so the total is the same on every run (a small kernel zeroes it first);
+//  * tq_gamma_kernel: one workgroup shifts the 255 totals into a 384-bit
+//    integer, rounds it to fp64 (nearest, ties to even), forms gamma and its
+//    fp16 bits, and a status (TQ_ERR_VALUE for a non-finite latent or gamma);
+//  * tq_pack_tq2_dev_kernel / tq_pack_tq1_dev_kernel: one output dword (16
+//    weights) or one TQ1 byte (5 weights) per thread, grid-stride.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+#include "tq_common.h"
+
+namespace {
+
+constexpr int kSumThreads = 256;
+constexpr int kSumWaves = kSumThreads / 64;
+constexpr int64_t kElemsPerGroup = int64_t(1) << 16;  // target elements per sum workgroup
+constexpr int64_t kMaxGroups = 2048;
+
+// Workspace layout: [info: 64 B][lo: uint64 [256]][hi: uint64 [256]][bad: int32].
+// info holds gamma (fp64), its fp16 bits and the status.
+struct Info {
+  double gamma;
+  uint32_t h;
+  int32_t status;
+};
+
+int64_t sum_groups(int64_t N, int64_t K) {
+  const int64_t total = N * K;
+  int64_t g = (total + kElemsPerGroup - 1) / kElemsPerGroup;
+  if (g < 1) g = 1;
+  if (g > kMaxGroups) g = kMaxGroups;
+  return g;
+}
+
+constexpr int64_t kLoOff = 64;
+constexpr int64_t kHiOff = kLoOff + 256 * 8;
+constexpr int64_t kBadOff = kHiOff + 256 * 8;
+constexpr int64_t kWorkspace = kBadOff + 64;
+
+__global__ void tq_sum_init_kernel(unsigned long long* lo, unsigned long long* hi, int* bad) {
+  const int e = threadIdx.x;
+  lo[e] = 0ull;
+  hi[e] = 0ull;
+  if (e == 0) *bad = 0;
+}
+
+__global__ __launch_bounds__(kSumThreads) void tq_abs_sum_kernel(const float* __restrict__ W,
+                                                                 int64_t total,
+                                                                 unsigned long long* lo,
+                                                                 unsigned long long* hi,
+                                                                 int* bad_out) {
+  __shared__ unsigned long long bk[kSumWaves][256];
+  __shared__ int bad;
+  for (int i = threadIdx.x; i < kSumWaves * 256; i += blockDim.x) (&bk[0][0])[i] = 0ull;
+  if (threadIdx.x == 0) bad = 0;
+  __syncthreads();
+  const int wave = threadIdx.x >> 6;
+  int my_bad = 0;
+  const int64_t q4 = total / 4;  // total is a multiple of 256
+  const float4* W4 = reinterpret_cast<const float4*>(W);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < q4;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 v = W4[i];
+    const float vs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t u = __float_as_uint(vs[t]);
+      const uint32_t e = (u >> 23) & 0xFFu;
+      uint32_t m = u & 0x7FFFFFu;
+      if (e == 0xFFu) my_bad = 1;
+      if (e) m |= 0x800000u;
+      atomicAdd(&bk[wave][e], (unsigned long long)m);
+    }
+  }
+  if (my_bad) atomicOr(&bad, 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+    unsigned long long s = 0;
+#pragma unroll
+    for (int w = 0; w < kSumWaves; ++w) s += bk[w][e];  // < 2^58: no overflow
+    if (s) {
+      const unsigned long long old = atomicAdd(&lo[e], s);
+      if (old + s < old) atomicAdd(&hi[e], 1ull);  // this add carried out of 64 bits
+    }
+  }
+  if (threadIdx.x == 0 && bad) atomicOr(bad_out, 1);
+}
+
+// 384-bit unsigned integer in 32-bit limbs (single-thread use).
+struct BigSum {
+  static constexpr int kLimbs = 12;
+  uint32_t limb[kLimbs];
+  __device__ void clear() {
+    for (int i = 0; i < kLimbs; ++i) limb[i] = 0;
+  }
+  __device__ void add_shifted(uint64_t v, int shift) {  // += v << shift
+    int li = shift / 32, bi = shift % 32;
+    uint32_t part[3];
+    part[0] = (uint32_t)(v << bi);
+    part[1] = (uint32_t)(bi ? (v >> (32 - bi)) : (v >> 32));
+    part[2] = (uint32_t)(bi ? (v >> (64 - bi)) : 0);
+    uint64_t carry = 0;
+    for (int i = li; i < kLimbs; ++i) {
+      const uint64_t p = i - li < 3 ? part[i - li] : 0;
+      const uint64_t s = (uint64_t)limb[i] + p + carry;
+      limb[i] = (uint32_t)s;
+      carry = s >> 32;
+      if (i - li >= 2 && carry == 0) break;
+    }
+  }
+  __device__ int top_bit() const {
+    for (int i = kLimbs - 1; i >= 0; --i)
+      if (limb[i]) return i * 32 + 31 - __clz(limb[i]);
+    return -1;
+  }
+  __device__ int bit(int b) const { return b < 0 ? 0 : (limb[b / 32] >> (b % 32)) & 1; }
+  __device__ bool any_below(int b) const {
+    if (b <= 0) return false;
+    const int full = b / 32;
+    for (int i = 0; i < full; ++i)
+      if (limb[i]) return true;
+    const int rem = b % 32;
+    return rem && (limb[full] & ((1u << rem) - 1));
+  }
+  // value * 2^scale_exp rounded to nearest even fp64
+  __device__ double to_double(int scale_exp) const {
+    const int h = top_bit();
+    if (h < 0) return 0.0;
+    uint64_t mant = 0;
+    int lo = h - 52;
+    for (int b = h; b >= (lo > 0 ? lo : 0); --b) mant = (mant << 1) | (uint64_t)bit(b);
+    if (lo < 0) return ldexp((double)mant, scale_exp);
+    const int guard = bit(lo - 1);
+    const bool sticky = any_below(lo - 1);
+    if (guard && (sticky || (mant & 1))) {
+      ++mant;
+      if (mant == (uint64_t(1) << 53)) {
+        mant >>= 1;
+        ++lo;
+      }
+    }
+    return ldexp((double)mant, lo + scale_exp);
+  }
+};
+
+// One round-to-nearest-even step from binary64 to binary16.
+__device__ uint16_t f64_to_f16_bits_dev(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint16_t sign = (uint16_t)((u >> 48) & 0x8000);
+  const int be = (int)((u >> 52) & 0x7FF);
+  const uint64_t mant = u & ((uint64_t(1) << 52) - 1);
+  if (be == 0x7FF) return sign | (mant ? 0x7E00 : 0x7C00);
+  if (be == 0) return sign;
+  int E = be - 1023;
+  const uint64_t sig = mant | (uint64_t(1) << 52);
+  const int shift = (E >= -14) ? 42 : 42 + (-14 - E);
+  if (shift >= 64) return sign;
+  uint64_t r = sig >> shift;
+  const uint64_t rem = sig & ((uint64_t(1) << shift) - 1);
+  const uint64_t half = uint64_t(1) << (shift - 1);
+  if (rem > half || (rem == half && (r & 1))) ++r;
+  if (E >= -14) {
+    if (r == (1u << 11)) {
+      r >>= 1;
+      ++E;
+    }
+    if (E > 15) return sign | 0x7C00;
+    return sign | (uint16_t)(((E + 15) << 10) | (r & 0x3FF));
+  }
+  return sign | (uint16_t)r;
+}
+
+__global__ __launch_bounds__(64) void tq_gamma_kernel(const unsigned long long* lo,
+                                                      const unsigned long long* hi,
+                                                      const int* bad, int64_t total, double eps,
+                                                      Info* info, double* gamma_out,
+                                                      int* status_out) {
+  if (threadIdx.x != 0) return;
+  BigSum s;
+  s.clear();
+  for (int e = 0; e < 255; ++e) {
+    const int shift = (e ? e : 1) - 1;  // m * 2^(e' - 150) = m * 2^(e' - 1) * 2^-149
+    if (lo[e]) s.add_shifted(lo[e], shift);
+    if (hi[e]) s.add_shifted(hi[e], shift + 64);
+  }
+  const double S = s.to_double(-149);
+  const double g = eps + S / (double)total;
+  const bool ok = !*bad && isfinite(g) && g > 0.0;
+  info->gamma = g;
+  info->h = f64_to_f16_bits_dev(g);
+  info->status = ok ? TQ_OK : TQ_ERR_VALUE;
+  if (gamma_out) *gamma_out = g;
+  if (status_out) *status_out = info->status;
+}
+
+// round(clip(w / gamma, -1, 1)) with ties to even, as the host decides it.
+__device__ __forceinline__ int trit_of(float w, double gamma) {
+  const double q = (double)w / gamma;
+  return (q > 0.5) - (q < -0.5);
+}
+
+// One dword of qs (16 weights = 4 bytes of a row) per thread; the thread of a
+// block's first dword writes the block's scale.
+__global__ __launch_bounds__(256) void tq_pack_tq2_dev_kernel(const float* __restrict__ W,
+                                                              int64_t N, int64_t K,
+                                                              const Info* info,
+                                                              uint32_t* __restrict__ qs,
+                                                              uint16_t* __restrict__ scales) {
+  const double gamma = info->gamma;
+  const uint16_t h = (uint16_t)info->h;
+  const int64_t words = N * (K / 16);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float4* src = reinterpret_cast<const float4*>(W + 16 * i);
+    uint32_t word = 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 v = src[c];
+      const float vs[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        word |= (uint32_t)(trit_of(vs[t], gamma) + 1) << (2 * (4 * c + t));
+    }
+    qs[i] = word;
+    if ((i & 15) == 0) scales[i >> 4] = h;  // 16 dwords per 256-weight block
+  }
+}
+
+// One TQ1 byte per thread: group g of row n holds weights 5 g .. 5 g + 4, the
+// first as the most significant base-3 digit, weights past K as zero trits;
+// bytes g >= ceil(K / 5) of the row are 0.
+__global__ __launch_bounds__(256) void tq_pack_tq1_dev_kernel(const float* __restrict__ W,
+                                                              int64_t N, int64_t K, int64_t ldq,
+                                                              const Info* info,
+                                                              uint8_t* __restrict__ qs,
+                                                              uint16_t* __restrict__ scales) {
+  const double gamma = info->gamma;
+  const uint16_t h = (uint16_t)info->h;
+  const int64_t G = (K + 4) / 5;
+  const int64_t bytes = N * ldq;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < bytes;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t n = i / ldq;
+    const int64_t g = i - n * ldq;
+    uint8_t b = 0;
+    if (g < G) {
+      const float* row = W + n * K;
+      unsigned code = 0;
+#pragma unroll
+      for (int j = 0; j < 5; ++j) {
+        const int64_t k = 5 * g + j;
+        const int t = k < K ? trit_of(row[k], gamma) : 0;
+        code = 3 * code + (unsigned)(t + 1);
+      }
+      b = (uint8_t)((code * 256 + 242) / 243);
+    }
+    qs[i] = b;
+  }
+  const int64_t ns = N * (K / 256);
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ns;
+       i += (int64_t)gridDim.x * blockDim.x)
+    scales[i] = h;
+}
+
+int check_dev(const float* W, int64_t N, int64_t K, const void* qs, const uint16_t* scales,
+              void* workspace, int64_t workspace_bytes_given) {
+  if (!W || !qs || !scales || !workspace) return TQ_ERR_NULL;
+  if (N < 1 || K < 256 || K % 256 || N > (int64_t(1) << 24) || K > (int64_t(1) << 20))
+    return TQ_ERR_SHAPE;
+  if (workspace_bytes_given < kWorkspace) return TQ_ERR_SHAPE;
+  if (((uintptr_t)W | (uintptr_t)qs | (uintptr_t)scales | (uintptr_t)workspace) & 15)
+    return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
+
+int have_device() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n < 1) {
+    (void)hipGetLastError();
+    return TQ_ERR_DEVICE;
+  }
+  return TQ_OK;
+}
+
+int launch_gamma(const float* W, int64_t N, int64_t K, double eps, double* gamma,
+                 int* status, unsigned char* ws, hipStream_t stream) {
+  if (have_device() != TQ_OK) return TQ_ERR_DEVICE;
+  auto* lo = reinterpret_cast<unsigned long long*>(ws + kLoOff);
+  auto* hi = reinterpret_cast<unsigned long long*>(ws + kHiOff);
+  int* bad = reinterpret_cast<int*>(ws + kBadOff);
+  Info* info = reinterpret_cast<Info*>(ws);
+  hipLaunchKernelGGL(tq_sum_init_kernel, dim3(1), dim3(256), 0, stream, lo, hi, bad);
+  hipLaunchKernelGGL(tq_abs_sum_kernel, dim3((unsigned)sum_groups(N, K)), dim3(kSumThreads), 0,
+                     stream, W, N * K, lo, hi, bad);
+  hipLaunchKernelGGL(tq_gamma_kernel, dim3(1), dim3(64), 0, stream, lo, hi, bad, N * K, eps,
+                     info, gamma, status);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
+}
+
+int pack_grid(int64_t items) {
+  int64_t g = (items + 255) / 256;
+  if (g > 8192) g = 8192;
+  return (int)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t tq_pack_dev_workspace_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 256 || K % 256) return -1;
+  return kWorkspace;
+}
+
+int tq_pack_tq2_dev(const float* W, int64_t N, int64_t K, double eps, uint8_t* qs,
+                    uint16_t* scales, double* gamma, int* status, void* workspace,
+                    int64_t workspace_bytes_given, void* stream) {
+  int st = check_dev(W, N, K, qs, scales, workspace, workspace_bytes_given);
+  if (st != TQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  st = launch_gamma(W, N, K, eps, gamma, status, ws, s);
+  if (st != TQ_OK) return st;
+  hipLaunchKernelGGL(tq_pack_tq2_dev_kernel, dim3(pack_grid(N * (K / 16))), dim3(256), 0, s, W,
+                     N, K, reinterpret_cast<const Info*>(ws), reinterpret_cast<uint32_t*>(qs),
+                     scales);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
+}
+
+int tq_pack_tq1_dev(const float* W, int64_t N, int64_t K, double eps, int64_t ldq, uint8_t* qs,
+                    uint16_t* scales, double* gamma, int* status, void* workspace,
+                    int64_t workspace_bytes_given, void* stream) {
+  int st = check_dev(W, N, K, qs, scales, workspace, workspace_bytes_given);
+  if (st != TQ_OK) return st;
+  if (ldq < (K + 4) / 5) return TQ_ERR_SHAPE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  st = launch_gamma(W, N, K, eps, gamma, status, ws, s);
+  if (st != TQ_OK) return st;
+  hipLaunchKernelGGL(tq_pack_tq1_dev_kernel, dim3(pack_grid(N * ldq)), dim3(256), 0, s, W, N, K,
+                     ldq, reinterpret_cast<const Info*>(ws), qs, scales);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
+}
+
+}  // extern "C"

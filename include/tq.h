@@ -153,6 +153,34 @@ int tq_gemm_tq2_ex(const void* X, const void* qs, const void* scales_f16, void* 
 int tq_gemm_tq1_ex(const void* X, const void* qs, int64_t ldq, const void* scales_f16, void* Y,
                    int64_t M, int64_t N, int64_t K, int path, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * On-device ternarization and packing (the step before the product; project
+ * page "The model" steps 1-2 and "Packing ternary weights").  The same
+ * results as tq_pack_tq2 / tq_pack_tq1 with TQ_SRC_LATENT_F32, bit for bit:
+ * gamma = eps + mean|W| with an exactly rounded fp64 sum of |W|, trits from
+ * the fp64 quotient W / gamma with ties to even, fp16(gamma) in every scale.
+ *
+ * W float [N][K], qs, scales, gamma (one double), status (one int) and the
+ * workspace are device memory on the current device; the call enqueues four
+ * kernels on `stream` and returns (no host round trip, no allocation).
+ * gamma and status may be NULL.  The workspace holds at least
+ * tq_pack_dev_workspace_bytes(N, K) bytes (a few KB); its contents need no
+ * initialization and are overwritten, so calls that may overlap need
+ * separate workspaces.  The exact sum uses 64-bit integer atomics, whose
+ * result does not depend on their order: every run gives the same bits.  W, qs, scales and the workspace must be
+ * 16-byte aligned.  Shapes: N >= 1, 256 <= K <= 2^20, K % 256 == 0, N <=
+ * 2^24; TQ1 ldq >= ceil(K/5).  Synchronous errors: TQ_ERR_NULL, TQ_ERR_SHAPE
+ * (also a workspace that is too small), TQ_ERR_ALIGN, TQ_ERR_DEVICE.  A
+ * non-finite latent or gamma is reported through *status (TQ_ERR_VALUE, else
+ * TQ_OK) once the stream reaches it; qs and scales are then unspecified. */
+int64_t tq_pack_dev_workspace_bytes(int64_t N, int64_t K); /* -1 for a bad shape */
+int tq_pack_tq2_dev(const float* W, int64_t N, int64_t K, double eps, uint8_t* qs,
+                    uint16_t* scales_f16, double* gamma, int* status, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+int tq_pack_tq1_dev(const float* W, int64_t N, int64_t K, double eps, int64_t ldq, uint8_t* qs,
+                    uint16_t* scales_f16, double* gamma, int* status, void* workspace,
+                    int64_t workspace_bytes, void* stream);
+
 /* TQ2 product on the tiled kernel with an explicit tile, for tuning and for
  * tests of every tile: 16 mt activation rows x 64 ng weight rows (32 ng when
  * mt = 8) per workgroup of ng x kg waves (kg of them split K).  Compiled

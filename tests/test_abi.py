@@ -105,6 +105,24 @@ def test_tq1_tiled_tile_errors():
     assert _gt1(3, 4, 4, X=None, M=0) == tq.TQ_OK
 
 
+def test_pack_dev_argument_errors():
+    wsb = tq.lib.tq_pack_dev_workspace_bytes(64, 512)
+    assert wsb > 256 * 8
+    assert tq.lib.tq_pack_dev_workspace_bytes(0, 512) == -1
+    assert tq.lib.tq_pack_dev_workspace_bytes(4, 300) == -1
+
+    def p2(W=A, N=64, K=512, q=A, s=A, ws=A, wsb=wsb):
+        return tq.raw_call("tq_pack_tq2_dev", W, N, K, 1e-5, q, s, None, None, ws, wsb, None)
+
+    assert p2(W=None) == tq.TQ_ERR_NULL
+    assert p2(ws=None) == tq.TQ_ERR_NULL
+    assert p2(K=300) == tq.TQ_ERR_SHAPE
+    assert p2(wsb=wsb - 8) == tq.TQ_ERR_SHAPE
+    assert p2(W=A + 4) == tq.TQ_ERR_ALIGN
+    assert tq.raw_call("tq_pack_tq1_dev", A, 64, 512, 1e-5, 96, A, A, None, None, A, wsb,
+                       None) == tq.TQ_ERR_SHAPE  # ldq < ceil(512 / 5)
+
+
 @pytest.mark.skipif(HAS_GPU, reason="checks the no-device error; a GPU is present")
 def test_gemm_without_device():
     assert _g2() == tq.TQ_ERR_DEVICE
