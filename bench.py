@@ -354,6 +354,103 @@ def pack_cpu_baseline(rows=64):
                       f"by N/{rows}", "s_tq2": round(res["tq2"], 3), "s_tq1": round(res["tq1"], 3)}
 
 
+# ----------------------------------------------------------------------------- layer stack
+
+# One decoder layer of the 80-layer stack, (name, K, N): 68.45 B weights, 17.65 GB TQ2.
+STACK_LAYER = [("q", 8192, 8192), ("k", 8192, 1024), ("v", 8192, 1024), ("o", 8192, 8192),
+               ("gate", 8192, 28672), ("up", 8192, 28672), ("down", 28672, 8192)]
+STACK_LAYERS = 80
+STACK_MS = [1, 16]
+
+
+def stack_bench(args):
+    """All 560 TQ2 linears of the stack, each with its own weights in HBM, back to
+    back in one HIP graph per M (activations random per linear shape)."""
+    import torch
+    import bit_mixed_precision_amd.binding as tq
+    from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    torch.cuda.set_device(0)
+    base = {}
+    for name, K, N in STACK_LAYER:
+        if (K, N) in base:
+            continue
+        rng = seed_for(800, K, N)
+        T = ternary_iid(rng, N, K, 0.31)
+        s = block_scales_fp16(rng, N, K)
+        base[(K, N)] = (torch.from_numpy(tq.tq_pack_tq2(T)[0]).cuda(), torch.from_numpy(s).cuda())
+        del T
+    weights = []  # every linear of every layer in its own buffers
+    for _ in range(STACK_LAYERS):
+        weights.append([(name, K, N, base[(K, N)][0].clone(), base[(K, N)][1].clone())
+                        for name, K, N in STACK_LAYER])
+    torch.cuda.synchronize()
+    log(f"[bench] stack: {STACK_LAYERS} layers x {len(STACK_LAYER)} linears in HBM")
+    results = []
+    stream = torch.cuda.current_stream()
+    for M in STACK_MS:
+        xs = {K: torch.from_numpy(activations_fp16(seed_for(801, M, K), M, K)).cuda()
+              for _, K, _ in STACK_LAYER}
+        ys = {N: torch.empty((M, N), dtype=torch.float16, device="cuda") for _, _, N in STACK_LAYER}
+
+        def step(sp):
+            for layer in weights:
+                for name, K, N, q, sc in layer:
+                    st = tq.lib.tq_gemm_tq2(xs[K].data_ptr(), q.data_ptr(), sc.data_ptr(),
+                                            ys[N].data_ptr(), M, N, K, sp)
+                    if st != 0:
+                        raise RuntimeError(tq.tq_status_string(st))
+
+        step(stream.cuda_stream)  # eager pass: kernel attributes outside capture
+        torch.cuda.synchronize()
+        cap = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                step(cap.cuda_stream)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // 4)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = STACK_LAYERS * sum(alg_bytes("tq2", M, N, K) for _, K, N in STACK_LAYER)
+        flops = STACK_LAYERS * sum(alg_flops(M, N, K) for _, K, N in STACK_LAYER)
+        roof = max(nbytes / HBM_PEAK, flops / MFMA_F16_PEAK)
+        results.append({"M": M, "ms_per_step": round(ms, 4), "TBps": round(nbytes / ms / 1e9, 3),
+                        "roofline_ms": round(roof * 1e3, 4), "roof_frac": round(roof * 1e3 / ms, 4)})
+        log(f"[bench] stack M={M}: {ms:.3f} ms per step ({nbytes / ms / 1e9:.2f} TB/s)")
+        del g
+    return results
+
+
+def stack_cpu_baseline(cols=256):
+    """The oracle on one layer (every linear on ``cols`` sampled output columns,
+    time scaled by N / cols), times 80 layers, at M = 1."""
+    from oracle import gemm_ref
+    from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
+    t_total = 0.0
+    for name, K, N in STACK_LAYER:
+        rng = seed_for(802, K)
+        T, s = ternary_iid(rng, cols, K, 0.31), block_scales_fp16(rng, cols, K)
+        X = activations_fp16(seed_for(803, 1, K), 1, K)
+        t = time.perf_counter()
+        gemm_ref(X, T, s)
+        t_total += (time.perf_counter() - t) * (N / cols)
+    t_step = t_total * STACK_LAYERS
+    nbytes = STACK_LAYERS * sum(alg_bytes("tq2", 1, N, K) for _, K, N in STACK_LAYER)
+    return {"value": round(nbytes / HBM_PEAK / t_step, 8), "unit": "fraction of HBM roofline",
+            "cores": os.cpu_count() or 1, "kind": "oracle",
+            "sample": f"one layer at M = 1, every linear on {cols} sampled output columns, time "
+                      f"scaled by N/{cols} and by {STACK_LAYERS} layers", "s_per_step": round(t_step, 3)}
+
+
 # ----------------------------------------------------------------------------- main
 
 def main():
@@ -364,6 +461,8 @@ def main():
     ap.add_argument("--reps", type=int, default=30, help="launches per call when timing each call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calls-out", default=None, help="also write the per-call table here (JSON)")
+    ap.add_argument("--stack", action="store_true",
+                    help="the 560 linears of an 80-layer stack, back to back in one HIP graph")
     ap.add_argument("--pack", action="store_true",
                     help="on-device ternarize + pack of a 28672 x 8192 latent matrix")
     ap.add_argument("--prefill", action="store_true",
@@ -374,6 +473,25 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
+    if args.stack:
+        rows = stack_bench(args)
+        m1 = rows[0]
+        out = {
+            "metric": "80-layer ternary stack: 560 TQ2 GEMMs per step vs HBM roofline (M = 1, 16)",
+            "value": m1["roof_frac"],
+            "unit": "fraction of roofline at M = 1 (HBM 8 TB/s)",
+            "n_gpus": 1, "steps": args.steps, "warmup": 2, "ms_per_step": m1["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "80 x {q 8192->8192, k/v 8192->1024, o 8192->8192, gate/up "
+                                   "8192->28672, down 28672->8192}, 17.65 GB TQ2, one HIP graph",
+                       "global_batch": None, "seq_len": None, "parallelism": "none"},
+            "per_M": rows,
+        }
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = stack_cpu_baseline()
+        print(json.dumps(out), flush=True)
+        return
     if args.pack:
         rows = pack_bench(args)
         t_roof_sum = sum(pack_bytes(2 if r["fmt"] == "tq2" else 1, r["N"], r["K"]) for r in rows)

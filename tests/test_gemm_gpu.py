@@ -278,6 +278,30 @@ def test_full_size_tq1(N, p):
         check_close(Y[:, cols], ref(X, T, s, cols=cols), f"full tq1 N={N} p={p} M={M}")
 
 
+# The seven linears of one layer of the 80-layer stack (K, N): q, k, v, o,
+# gate, up, down.
+STACK_LINEARS = {"q": (8192, 8192), "kv": (8192, 1024), "gate_up": (8192, 28672),
+                 "down": (28672, 8192)}
+
+
+@pytest.mark.parametrize("fmt", ["tq2", "tq1"])
+@pytest.mark.parametrize("name", list(STACK_LINEARS))
+def test_stack_layer_shapes(fmt, name):
+    """Every distinct linear shape of the stack at M = 1 and 16 on the automatic
+    kernel choice: 128 sampled columns against the oracle, all outputs finite."""
+    K, N = STACK_LINEARS[name]
+    T, s = iid_problem(N, K, 0.31, 90)
+    q = pack(fmt, T)
+    cols = np.sort(seed_for(91, N).choice(N, 128, replace=False))
+    cols[0], cols[-1] = 0, N - 1
+    for M in (1, 16):
+        say(f"[stack] {fmt} {name} M={M} K={K} N={N}")
+        X = activations(M, K, 90 + M)
+        Y = run(fmt, X, q, s, "auto").cpu().numpy()
+        assert np.all(np.isfinite(Y.astype(np.float32)))
+        check_close(Y[:, cols], ref(X, T, s, cols=cols), f"stack {fmt} {name} M={M}")
+
+
 PREFILL = [(256, 8192), (1024, 8192), (4096, 8192), (256, 28672)]
 
 
