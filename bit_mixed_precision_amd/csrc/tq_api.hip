@@ -82,7 +82,7 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
                       tq::tq1_stage(N, K), tq::tq1_slices(M)};
       if (M > kSkinnyMaxM) return Choice{nullptr, "", -1, -1};
       return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_depth(),
-                    tq::skinny_stage(N, K)};
+                    tq::skinny_stage(N, K, M)};
     case TQ_PATH_TILED: {
       if (tq1) {
         const tq::Tq1TiledShape t = tq::tq1_tiled_shape(M, N);

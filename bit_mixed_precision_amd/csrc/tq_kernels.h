@@ -27,7 +27,7 @@ hipError_t launch_tq1_simple(const GemmArgs& a, hipStream_t stream);
 // groups one workgroup owns (the template argument of the kernel).
 int skinny_rows(int64_t N);
 int skinny_depth();                      // register ring depth (template argument)
-int skinny_stage(int64_t N, int64_t K);  // 1 when block scales are staged in LDS
+int skinny_stage(int64_t N, int64_t K, int64_t M);  // 1 when block scales are staged in LDS
 hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream);
 
 // TQ1 MFMA kernel: any M, in slices of 16 activation rows.

@@ -281,8 +281,6 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
             const int e = threadIdx.x + r * T;
             if (e < ns) sc_lds[e] = h2f(sreg[r]);
           }
-          for (int e = threadIdx.x + kScaleRegs * T; e < ns; e += T)
-            sc_lds[e] = h2f(ssrc[e]);
         }
       }
     }
@@ -363,8 +361,14 @@ int skinny_rows(int64_t N) { return pick_rows(N, device_cus()); }
 
 int skinny_depth() { return kDepth; }
 
-int skinny_stage(int64_t N, int64_t K) {
-  return scale_lds_bytes(skinny_rows(N), K) <= kScaleLdsMax ? 1 : 0;
+int skinny_lwk(int64_t N, int64_t K, int64_t M);
+
+int skinny_stage(int64_t N, int64_t K, int64_t M) {
+  const int64_t RG = skinny_rows(N);
+  const int64_t threads = 64 * (RG << skinny_lwk(N, K, M));
+  return scale_lds_bytes(RG, K) <= kScaleLdsMax && 16 * RG * (K / 256) <= kScaleRegs * threads
+             ? 1
+             : 0;
 }
 
 // Waves per row group: 2^lwk (a power of two, so the kernel's K slicing is
@@ -395,7 +399,8 @@ hipError_t launch_tq2_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk)
   int xregion = xbytes > W * 1024 ? xbytes : W * 1024;  // also holds the reduction
   xregion = (xregion + 15) & ~15;
   const int64_t sbytes = scale_lds_bytes(RG, K);
-  const bool stage = sbytes <= kScaleLdsMax;
+  // staged: every thread holds at most kScaleRegs of the workgroup's scales
+  const bool stage = sbytes <= kScaleLdsMax && int64_t{16} * RG * nb <= int64_t{kScaleRegs} * 64 * W;
   const int lds = xregion + (stage ? (int)sbytes : 0);
   if (lds > kLdsLimit) return hipErrorInvalidValue;
   return stage ? launch_tq2_skinny_s<true>(a, stream, RG, lwk, nbw, xregion, lds)

@@ -10,9 +10,11 @@
 // inference on GPUs" for FP32 accumulation and FP16 output.  MI355X design:
 //
 //  * two weight bytes sit in the two 16-bit halves of a register, so each
-//    step of the decoder (t = 3 q with v_lshl_add_u32, digit = t >> 8 taken
-//    straight into an fp16 mantissa with v_and_or_b32 against the exponent of
-//    1024, one v_pk_fma_f16 to get the trit, q = t & 0xff) serves two weights;
+//    step of the decoder (t = 3 q with v_lshl_add_u32, the digit field of t
+//    kept by one v_and_b32, q = t & 0xff) serves two weights.  The kept field
+//    d' 256 is an fp16 subnormal worth d' 2^-16, which the MFMA multiplies
+//    exactly (it keeps subnormals); the shift d = d' - 1 is the sum of the
+//    activations, taken in fp32 while staging them, seeding the accumulator;
 //  * v_mfma_f32_16x16x32_f16 does the multiply-accumulate with 16 activation
 //    rows per launch slice (grid.y walks M in slices of 16);
 //  * the four lane groups of a wave cover one 32-byte span of a row (160
@@ -22,9 +24,11 @@
 //    only, the span adds s_a C_a + (s_b - s_a) C_b: exact block scales
 //    without per-weight work.  C_b comes from a masked copy of the
 //    activations (zero before the boundary) kept next to the plain copy;
-//  * both activation copies are staged in LDS in the decoder's weight order;
-//    waves of a workgroup take spans round robin and keep a ring of register
-//    buffers of weights in flight; partial sums meet in LDS.
+//  * both activation copies, with their sums, are staged in LDS in the
+//    decoder's weight order; waves of a workgroup take spans round robin and
+//    keep a ring of register buffers of weights in flight (the last ring group
+//    issues no loads); per-wave set-up is kept to shifts and masks; partial
+//    sums meet in LDS.
 
 #include <type_traits>
 
@@ -46,75 +50,139 @@ __device__ __forceinline__ void sfor1(F&& f) {
 
 constexpr int kPad = 16;
 constexpr int kXLds = 128 * 1024;   // activation window budget
-constexpr int kScLds = 24 * 1024;   // staged scales budget
+constexpr int kScLds = 24 * 1024;   // staged scales budget (fp32)
 constexpr int kLdsMax = 160 * 1024;
+constexpr int kRowsMax = 32;        // activation rows of a workgroup (two 16-row slices)
+constexpr int kSumBytes = 2 * kRowsMax * 4;  // per span: plain and masked row sums, fp32
+constexpr int kTrash = (kUnitBytes + 4 * (kRowsMax + 1) + 15) & ~15;  // a unit's operands, sums
+constexpr int kScaleRegs = 4;                // block scales per thread loaded ahead
 // Activations in LDS, decoder order: for every (row m, span u, lane group g,
 // operand o) 8 halves.  o < 5: plain X at the operand's weights (zero past K);
 // o >= 5: the same masked to the weights at or past the span's block boundary.
-// A window holds spans [u0, u0 + nu) of rows m_base .. m_base + mrows - 1;
-// thread q stages unit q = (m, u, g) of every window (units <= threads): the
-// 40 consecutive activations k0 = 160 (u0 + u) + 40 g .. k0 + 39, read with
-// five coalesced 16-byte loads (K and k0 are multiples of 8, so a chunk is
-// either wholly inside the row or wholly past K) one window ahead, then
-// written with one v_perm_b32 per operand dword.
-__device__ __forceinline__ void tq1_load_unit(uint32_t (&e)[20], const uint16_t* __restrict__ X,
-                                              int m_base, int K, int u0, int nu, int q) {
-  const int g = q & 3;
-  const int u = (q >> 2) % nu;
-  const int m = (q >> 2) / nu;
-  const int k0 = 160 * (u0 + u) + 40 * g;
-  const uint16_t* xrow = X + (size_t)(m_base + m) * K;
+// Next to them, per span, -2^-16 times the sum over the span of each row's
+// plain and masked activations.  A window holds spans [u0, u0 + nu) of rows
+// m_base .. m_base + mrows - 1; thread q stages unit q = (m, u, g) of every
+// window (units <= threads): the 40 consecutive activations k0 = 160 (u0 + u)
+// + 40 g .. k0 + 39, read with five coalesced 16-byte loads (K and k0 are
+// multiples of 8, so a chunk is either wholly inside the row or wholly past
+// K) one window ahead, then written with one v_perm_b32 per operand dword.
+struct Tq1Unit {
+  uint32_t e[20];
+  int m, u;
+  int k0;  // first activation of the unit
+  bool ok;
+};
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+
+// Position of unit q in a window of nuw spans: u + nuw m = q / 4 (float
+// reciprocal: exact for q / 4 < 2^11), no integer division.
+__device__ __forceinline__ void tq1_unit_at(Tq1Unit& un, int q, int nuw, int mrows) {
+  const int r = q >> 2;
+  const int m = (int)(((float)r + 0.5f) * (1.0f / (float)nuw));
+  un.ok = m < mrows;
+  un.m = un.ok ? m : 0;
+  un.u = un.ok ? r - m * nuw : 0;
+}
+
+// Loads only (chunks past K re-read the row's first chunk; the store zeroes
+// them), so that nothing waits for the loads before the store.
+__device__ __forceinline__ void tq1_load_unit(Tq1Unit& un, const uint16_t* __restrict__ X,
+                                              int m_base, int K, int u0, int g) {
+  un.k0 = 160 * (u0 + un.u) + 40 * g;
+  const uint16_t* xrow = X + (size_t)(m_base + un.m) * K;
 #pragma unroll
   for (int c = 0; c < 5; ++c) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (k0 + 8 * c + 8 <= K) v = *reinterpret_cast<const u32x4*>(xrow + k0 + 8 * c);
+    const int k = un.k0 + 8 * c;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xrow + (k + 8 <= K ? k : 0));
 #pragma unroll
-    for (int t = 0; t < 4; ++t) e[4 * c + t] = v[t];
+    for (int t = 0; t < 4; ++t) un.e[4 * c + t] = v[t];
   }
 }
 
-__device__ __forceinline__ void tq1_store_unit(unsigned char* xs, const uint32_t (&e)[20], int u0,
-                                               int nu, int q, int xstride) {
-  const int g = q & 3;
-  const int u = (q >> 2) % nu;
-  const int m = (q >> 2) / nu;
-  const int k0 = 160 * (u0 + u) + 40 * g;
-  const int kb = ((160 * (u0 + u)) / 256 + 1) * 256;  // first block boundary of the span
-  tq1_store_operands(xs + m * xstride + u * kSpanBytes + g * kUnitBytes, e, kb - k0);
+// Writes the unit's ten operands (tq1_store_operands' layout) and, after a
+// sum over the four lane groups of its span, the span's row sums.
+__device__ __forceinline__ void tq1_store_unit(const Tq1Unit& un, unsigned char* xs, float* sums,
+                                               unsigned char* trash, int u0, int g, int xstride,
+                                               int K) {
+  const int k0 = un.k0;
+  uint32_t e[20];
+#pragma unroll
+  for (int c = 0; c < 5; ++c)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) e[4 * c + t] = k0 + 8 * c + 8 <= K ? un.e[4 * c + t] : 0u;
+  const int kb = (((160 * (u0 + un.u)) >> 8) + 1) << 8;  // first block boundary of the span
+  const int lim = kb - k0;
+  unsigned char* dst = un.ok ? xs + un.m * xstride + un.u * kSpanBytes + g * kUnitBytes : trash;
+  const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
+  float sa = 0.f, sb = 0.f;
+#pragma unroll
+  for (int j = 0; j < 5; ++j) {
+    u32x4 plain, masked;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      // slot pair (2t, 2t + 1) holds activations a = 5 byte(2t) + j, b = 5 byte(2t+1) + j
+      const int a = 5 * kByteOfSlot[2 * t] + j;
+      const int b = 5 * kByteOfSlot[2 * t + 1] + j;
+      const uint32_t sel = ((b & 1) ? 0x07060000u : 0x05040000u) | ((a & 1) ? 0x0302u : 0x0100u);
+      plain[t] = perm(e[b >> 1], e[a >> 1], sel);
+      const uint32_t keep = (a >= lim ? 0x0000FFFFu : 0u) | (b >= lim ? 0xFFFF0000u : 0u);
+      masked[t] = plain[t] & keep;
+      // (a bit cast of a vector element itself reads element 0: copy first)
+      const uint32_t pv = plain[t], mv = masked[t];
+      sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, pv), ones, sa, false);
+      sb = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, mv), ones, sb, false);
+    }
+    *reinterpret_cast<u32x4*>(dst + 16 * j) = plain;
+    *reinterpret_cast<u32x4*>(dst + 16 * (5 + j)) = masked;
+  }
+  sa += dpp_f32<0xB1>(sa);  // quad_perm [1, 0, 3, 2]: the span's four lane groups
+  sb += dpp_f32<0xB1>(sb);
+  sa += dpp_f32<0x4E>(sa);  // quad_perm [2, 3, 0, 1]
+  sb += dpp_f32<0x4E>(sb);
+  float* sd = un.ok ? sums + un.u * (2 * kRowsMax) + un.m : reinterpret_cast<float*>(trash + kUnitBytes);
+  if (g == 0) {
+    sd[0] = sa * -0x1p-16f;
+    sd[kRowsMax] = sb * -0x1p-16f;
+  }
 }
 
 template <int D, bool STAGE, int MS>
 __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ qs, int ldq,
     const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int M, int N, int K, int RG,
-    int WK, int nuw, int xregion) {
+    int lwk, int nuw, int xregion) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int li = lane & 15;
   const int g = lane >> 4;
   const int nb = K >> 8;
-  const int rg = wave / WK;
-  const int wk = wave % WK;
+  const int WK = 1 << lwk;
+  const int W = RG << lwk;
+  const int T = 64 * W;
+  const int rg = wave >> lwk;
+  const int wk = wave & (WK - 1);
   const int n_base = blockIdx.x * (16 * RG);
   const int rows = min(16 * RG, N - n_base);
   const int m_base = blockIdx.y * 16 * MS;  // MS slices of 16 activation rows
   const int mrows = min(16 * MS, M - m_base);
   const int groups = (K + 4) / 5;
-  const int nu = (groups + 31) / 32;  // 32-byte spans holding real bytes
+  const int nu = (groups + 31) >> 5;  // 32-byte spans holding real bytes
   const int xstride = nuw * kSpanBytes + kPad;
-  uint16_t* sc_lds = reinterpret_cast<uint16_t*>(smem + xregion);
-
-  Tq1Decoder dc;
-  dc.init();
+  float* sums = reinterpret_cast<float*>(smem + mrows * xstride);
+  unsigned char* trash = reinterpret_cast<unsigned char*>(sums + nuw * 2 * kRowsMax);
+  float* sc_lds = reinterpret_cast<float*>(smem + xregion);
 
   const int nrow = 16 * rg + li < rows ? 16 * rg + li : 0;
   const uint8_t* wrow = qs + (size_t)(n_base + nrow) * ldq + 8 * g;
   const uint16_t* srow_g = scales + (size_t)(n_base + nrow) * nb;
-  if constexpr (STAGE) {
-    const uint16_t* src = scales + (size_t)n_base * nb;
-    for (int i = threadIdx.x; i < rows * nb; i += blockDim.x) sc_lds[i] = src[i];
-  }
+  const int ns = STAGE ? rows * nb : 0;
+  const uint16_t* ssrc = scales + (size_t)n_base * nb;
   // Activation row of this lane in slice ms (rows past M repeat the last one;
   // their results are never written).
   const unsigned char* xa[MS];
@@ -138,30 +206,37 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
   auto scale_at = [&](int b) -> float {
-    if constexpr (STAGE) return h2f(sc_lds[nrow * nb + b]);
+    if constexpr (STAGE) return sc_lds[nrow * nb + b];
     return h2f(srow_g[b]);
   };
   auto compute = [&](int d, int u, int uw) {
     const u32x2 w = wbuf[d];
     // bytes (0, 2), (1, 3), (4, 6), (5, 7) of the lane's 8 bytes, one per half
-    uint32_t q[4] = {w[0] & 0x00FF00FFu, (w[0] >> 8) & 0x00FF00FFu, w[1] & 0x00FF00FFu,
-                     (w[1] >> 8) & 0x00FF00FFu};
+    uint32_t q[4] = {perm(0u, w[0], 0x0C020C00u), perm(0u, w[0], 0x0C030C01u),
+                     perm(0u, w[1], 0x0C020C00u), perm(0u, w[1], 0x0C030C01u)};
     const int ba = (160 * u) >> 8;
     const float sa = scale_at(ba < nb ? ba : nb - 1);
     // A span holds a block boundary (and a second scale) only when the next
     // block starts before the span ends; otherwise the masked product is zero.
     const bool split = 256 * (ba + 1) < 160 * (u + 1) && ba + 1 < nb;  // wave-uniform
+    const float* su = sums + uw * (2 * kRowsMax) + 4 * g;
     auto run = [&](auto with_b) {
       constexpr bool WB = decltype(with_b)::value;
       float4v Ca[MS], Cb[MS];
 #pragma unroll
-      for (int ms = 0; ms < MS; ++ms) Ca[ms] = Cb[ms] = float4v{0.f, 0.f, 0.f, 0.f};
-      uint32_t qq[4] = {q[0], q[1], q[2], q[3]};
+      for (int ms = 0; ms < MS; ++ms) {
+        Ca[ms] = *reinterpret_cast<const float4v*>(su + 16 * ms);  // -2^-16 (row sums)
+        if constexpr (WB) Cb[ms] = *reinterpret_cast<const float4v*>(su + kRowsMax + 16 * ms);
+      }
       sfor1<0, 5>([&](auto jj) {
         constexpr int j = decltype(jj)::value;
         u32x4 b;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b[i] = dc.step(qq[i]);
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t t = (q[i] << 1) + q[i];  // no carry between halves: 3 * 255 < 2^16
+          b[i] = t & 0x03000300u;                 // digit d' at bits 8..9: d' 2^-16
+          q[i] = t & 0x00FF00FFu;
+        }
         const half8 B = __builtin_bit_cast(half8, b);  // decoded once, used by every slice
 #pragma unroll
         for (int ms = 0; ms < MS; ++ms) {
@@ -189,51 +264,88 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
       run(std::false_type{});
   };
 
-  // This thread's staging unit, one window ahead (units <= threads).
+  // This thread's staging unit, loaded one window ahead (units <= threads).
   const int q = threadIdx.x;
-  uint32_t xe[20];
-  if (q < mrows * min(nuw, nu) * 4) tq1_load_unit(xe, X, m_base, K, 0, min(nuw, nu), q);
+  Tq1Unit un;
+  tq1_unit_at(un, q, min(nuw, nu), mrows);
+  tq1_load_unit(un, X, m_base, K, 0, q & 3);
+  // block scales: read with the first window's activations, before the
+  // weight prefetch
+  uint16_t sreg[kScaleRegs];
+  if constexpr (STAGE) {
+#pragma unroll
+    for (int r = 0; r < kScaleRegs; ++r) {
+      const int e = threadIdx.x + r * T;
+      sreg[r] = ssrc[e < ns ? e : 0];
+    }
+  }
   for (int u0 = 0; u0 < nu; u0 += nuw) {
     const int nuw_here = min(nuw, nu - u0);
-    const int cnt = nuw_here > wk ? (nuw_here - wk + WK - 1) / WK : 0;
-    auto span = [&](int i) { return u0 + wk + WK * (i < cnt ? i : cnt - 1); };
-    if (cnt > 0) {
-      sfor1<0, D>([&](auto dd) { load(decltype(dd)::value, span(decltype(dd)::value)); });
-    }
+    const int cnt = nuw_here > wk ? (nuw_here - wk + WK - 1) >> lwk : 0;
+    auto span = [&](int i) { return cnt > 0 ? u0 + wk + WK * (i < cnt ? i : cnt - 1) : u0; };
+    sfor1<0, D>([&](auto dd) { load(decltype(dd)::value, span(decltype(dd)::value)); });
     __syncthreads();  // the previous window is consumed
-    if (q < mrows * nuw_here * 4) tq1_store_unit(smem, xe, u0, nuw_here, q, xstride);
-    const int u1 = u0 + nuw;  // the next window's activations fly during this one
-    if (u1 < nu && q < mrows * min(nuw, nu - u1) * 4)
-      tq1_load_unit(xe, X, m_base, K, u1, min(nuw, nu - u1), q);
+    tq1_store_unit(un, smem, sums, trash, u0, q & 3, xstride, K);
+    if constexpr (STAGE) {
+      if (u0 == 0) {
+#pragma unroll
+        for (int r = 0; r < kScaleRegs; ++r) {
+          const int e = threadIdx.x + r * T;
+          uint32_t v = sreg[r];
+          asm volatile("" : "+v"(v));  // convert here, not ahead of the loop (no early wait)
+          if (e < ns) sc_lds[e] = h2f((uint16_t)v);
+        }
+      }
+    }
     __syncthreads();
-    for (int i = 0; i < cnt; i += D) {
+    // First group.  The next window's activations are loaded after its first
+    // step (after the last window a harmless re-read of this one), so they
+    // are older than every weight load in flight in the loop below: the
+    // compiler's wait before each step then covers exactly the oldest ring
+    // buffer, on entry as on every later pass.
+    sfor1<0, D>([&](auto dd) {
+      constexpr int d = decltype(dd)::value;
+      if (d < cnt) compute(d, span(d), wk + WK * d);
+      if constexpr (d == 0) {
+        const int u1 = u0 + nuw < nu ? u0 + nuw : u0;
+        tq1_unit_at(un, q, min(nuw, nu - u1), mrows);
+        tq1_load_unit(un, X, m_base, K, u1, q & 3);
+      }
+      load(d, span(d + D));
+    });
+    int i = D;
+    for (; i + D < cnt; i += D) {
       sfor1<0, D>([&](auto dd) {
         constexpr int d = decltype(dd)::value;
-        if (i + d < cnt) compute(d, span(i + d), wk + WK * (i + d));
+        compute(d, span(i + d), wk + WK * (i + d));
         load(d, span(i + d + D));
       });
     }
+    // last group: no loads past the wave's spans
+    sfor1<0, D>([&](auto dd) {
+      constexpr int d = decltype(dd)::value;
+      if (i + d < cnt) compute(d, span(i + d), wk + WK * (i + d));
+    });
   }
 
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
-  const int nw = RG * WK;  // waves of the workgroup
 #pragma unroll
   for (int ms = 0; ms < MS; ++ms)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) red[(ms * nw + wave) * 256 + i * 64 + lane] = acc[ms][i];
+    for (int i = 0; i < 4; ++i) red[(ms * W + wave) * 256 + i * 64 + lane] = acc[ms][i];
   __syncthreads();
-  for (int t = threadIdx.x; t < MS * RG * 256; t += blockDim.x) {
-    const int ms = t / (RG * 256);
-    const int r = (t >> 8) % RG;
+  for (int t = threadIdx.x; t < MS * RG * 256; t += T) {
+    const int ms = MS == 1 ? 0 : t / (RG * 256);
+    const int r = (t >> 8) - ms * RG;
     const int e = t & 255;
     const int l = e & 63;
     const int m = 16 * ms + 4 * (l >> 4) + (e >> 6);
     const int n = 16 * r + (l & 15);
     if (m < mrows && n < rows) {
       float sum = 0.f;
-      for (int k = 0; k < WK; ++k) sum += red[(ms * nw + r * WK + k) * 256 + e];
-      Y[(size_t)(m_base + m) * N + n_base + n] = f2h_bits(sum);
+      for (int k = 0; k < WK; ++k) sum += red[(ms * W + r * WK + k) * 256 + e];
+      Y[(size_t)(m_base + m) * N + n_base + n] = f2h_bits(sum * 0x1p16f);
     }
   }
 }
@@ -242,7 +354,7 @@ constexpr int kDepth1 = 3;
 
 template <bool STAGE, int MS>
 hipError_t launch_tq1_s(const GemmArgs& a, hipStream_t stream, dim3 grid, int W, int lds, int RG,
-                        int WK, int nuw, int xregion) {
+                        int lwk, int nuw, int xregion) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e =
@@ -254,17 +366,19 @@ hipError_t launch_tq1_s(const GemmArgs& a, hipStream_t stream, dim3 grid, int W,
   hipLaunchKernelGGL((tq1_skinny_kernel<kDepth1, STAGE, MS>), grid, dim3(64 * W), lds, stream,
                      static_cast<const uint16_t*>(a.X), static_cast<const uint8_t*>(a.qs),
                      (int)a.ldq, static_cast<const uint16_t*>(a.scales),
-                     static_cast<uint16_t*>(a.Y), (int)a.M, (int)a.N, (int)a.K, RG, WK, nuw,
+                     static_cast<uint16_t*>(a.Y), (int)a.M, (int)a.N, (int)a.K, RG, lwk, nuw,
                      xregion);
   return hipGetLastError();
 }
 
 template <bool STAGE>
 hipError_t launch_tq1_ms(int ms, const GemmArgs& a, hipStream_t stream, dim3 grid, int W, int lds,
-                         int RG, int WK, int nuw, int xregion) {
-  if (ms == 2) return launch_tq1_s<STAGE, 2>(a, stream, grid, W, lds, RG, WK, nuw, xregion);
-  return launch_tq1_s<STAGE, 1>(a, stream, grid, W, lds, RG, WK, nuw, xregion);
+                         int RG, int lwk, int nuw, int xregion) {
+  if (ms == 2) return launch_tq1_s<STAGE, 2>(a, stream, grid, W, lds, RG, lwk, nuw, xregion);
+  return launch_tq1_s<STAGE, 1>(a, stream, grid, W, lds, RG, lwk, nuw, xregion);
 }
+
+int64_t tq1_scale_bytes(int64_t RG, int64_t K) { return ((16 * RG * (K / 256) * 4) + 15) & ~15; }
 
 }  // namespace
 
@@ -272,43 +386,57 @@ int tq1_depth() { return kDepth1; }
 
 int tq1_slices(int64_t M) { return M <= 16 ? 1 : 2; }
 
+int tq1_lwk(int64_t N, int64_t K);
+
 int tq1_stage(int64_t N, int64_t K) {
   const int64_t RG = skinny_rows(N);
-  const int64_t sbytes = ((16 * RG * (K / 256) * 2) + 15) & ~15;
-  return sbytes <= kScLds ? 1 : 0;
+  const int64_t threads = 64 * (RG << tq1_lwk(N, K));
+  return tq1_scale_bytes(RG, K) <= kScLds && 16 * RG * (K / 256) <= kScaleRegs * threads ? 1 : 0;
 }
 
-hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream) {
+// Waves per row group: 2^lwk, at most 16 waves per workgroup and no more than
+// there are spans.
+int tq1_lwk(int64_t N, int64_t K) {
+  const int RG = skinny_rows(N);
+  const int64_t nu = ((K + 4) / 5 + 31) / 32;
+  int lwk = 0;
+  while ((RG << (lwk + 1)) <= 16 && (int64_t{2} << lwk) <= nu) ++lwk;
+  return lwk;
+}
+
+hipError_t launch_tq1_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk) {
   const int M = (int)a.M, K = (int)a.K;
-  const int nb = K / 256;
   const int groups = (K + 4) / 5;
   const int nu = (groups + 31) / 32;
   const int RG = skinny_rows(a.N);
-  int WK = 16 / RG;
-  if (WK > nu) WK = nu;
-  if (WK < 1) WK = 1;
-  const int W = RG * WK;
+  const int W = RG << lwk;
+  if (lwk < 0 || W > 16) return hipErrorInvalidValue;
   // Activation slices per workgroup: every weight is decoded once per
   // workgroup, so a workgroup takes up to 32 activation rows (more rows give
   // no gain: past that the activation reads from LDS, one per MFMA, bound it,
   // and the 1024-thread workgroup runs out of registers).
   const int ms = tq1_slices(M);
   const int mrows = M < 16 * ms ? M : 16 * ms;
-  int nuw = (kXLds / mrows - kPad) / kSpanBytes;
+  int nuw = (kXLds - mrows * kPad - kTrash) / (mrows * kSpanBytes + kSumBytes);
   if (nuw > nu) nuw = nu;
   if (nuw > 64 * W / (4 * mrows)) nuw = 64 * W / (4 * mrows);  // one staging unit per thread
   if (nuw < 1) return hipErrorInvalidValue;
-  const int xbytes = mrows * (nuw * kSpanBytes + kPad);
+  const int xbytes = mrows * (nuw * kSpanBytes + kPad) + nuw * kSumBytes + kTrash;
   const int rbytes = ms * W * 1024;  // the partial sums reuse the window
   int xregion = xbytes > rbytes ? xbytes : rbytes;
   xregion = (xregion + 15) & ~15;
-  const int sbytes = ((16 * RG * nb * 2) + 15) & ~15;
-  const bool stage = sbytes <= kScLds;
-  const int lds = xregion + (stage ? sbytes : 0);
+  const int64_t sbytes = tq1_scale_bytes(RG, K);
+  // staged: every thread holds at most kScaleRegs of the workgroup's scales
+  const bool stage = sbytes <= kScLds && int64_t{16} * RG * (K / 256) <= int64_t{kScaleRegs} * 64 * W;
+  const int lds = xregion + (stage ? (int)sbytes : 0);
   if (lds > kLdsMax) return hipErrorInvalidValue;
   dim3 grid((unsigned)((a.N + 16 * RG - 1) / (16 * RG)), (unsigned)((a.M + 16 * ms - 1) / (16 * ms)));
-  return stage ? launch_tq1_ms<true>(ms, a, stream, grid, W, lds, RG, WK, nuw, xregion)
-               : launch_tq1_ms<false>(ms, a, stream, grid, W, lds, RG, WK, nuw, xregion);
+  return stage ? launch_tq1_ms<true>(ms, a, stream, grid, W, lds, RG, lwk, nuw, xregion)
+               : launch_tq1_ms<false>(ms, a, stream, grid, W, lds, RG, lwk, nuw, xregion);
+}
+
+hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream) {
+  return launch_tq1_skinny_lwk(a, stream, tq1_lwk(a.N, a.K));
 }
 
 }  // namespace tq

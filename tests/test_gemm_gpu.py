@@ -3,7 +3,7 @@
 Bar: max|Y - Y_ref| <= 4e-3 * max|Y_ref| (Y is the fp16 GPU output widened to
 fp64); exact equality where the product is exactly representable (identity,
 permutations, one weight per row, zero weights), except for the stated fp32
-rounding of the folded d' = d + 1 offset on the TQ2 skinny path.  Every kernel family is forced
+rounding of the folded d' = d + 1 offset on the skinny paths.  Every kernel family is forced
 at every M through the *_ex entry points, so both sides of the M switch are
 covered.
 """
@@ -155,13 +155,13 @@ def ulp16(v):
 
 
 def same_or_offset_bound(Y, want, X, smax, fmt, path, bits=True):
-    """Bit-exact, except on the TQ2 skinny path: its decode leaves the stored
-    field d' = d + 1 and subtracts the block sums of the activations in fp32,
-    so a result carries the rounding of that cancellation, at most
-    2^-16 * max|s| * sum_k |x[m, k]| per row m (the derivation gives 2^-19),
-    besides the fp16 rounding of the output."""
+    """Bit-exact, except on the skinny paths: their decoders leave the stored
+    digit d' = d + 1 and subtract the block (TQ2) or span (TQ1) sums of the
+    activations in fp32, so a result carries the rounding of that
+    cancellation, at most 2^-16 * max|s| * sum_k |x[m, k]| per row m (the
+    derivation gives about 2^-19), besides the fp16 rounding of the output."""
     Y64, want64 = Y.astype(np.float64), np.asarray(want, np.float64)
-    if not (fmt == "tq2" and path == "skinny"):
+    if path != "skinny":
         if bits:  # same fp16 bit patterns (+0 where want is +0)
             assert np.array_equal(Y.view(np.uint16), np.asarray(want, np.float16).view(np.uint16))
         else:  # same values (either sign of zero)
@@ -176,7 +176,7 @@ def same_or_offset_bound(Y, want, X, smax, fmt, path, bits=True):
 @pytest.mark.parametrize("fmt", ["tq2", "tq1"])
 def test_exact_special_cases(fmt, path):
     """Identity, minus identity, permutation, zero, one weight per row: exact
-    (up to the stated offset rounding on the TQ2 skinny path)."""
+    (up to the stated offset rounding on the skinny paths)."""
     need(fmt, path)
     K = 512
     for M in (1, 5, 16, 40):
