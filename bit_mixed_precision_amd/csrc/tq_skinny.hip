@@ -273,7 +273,9 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
         }
       }
       static_for<0, D>([&](auto dd) { load(decltype(dd)::value, blk(decltype(dd)::value)); });
-      piece_store(v, ok, pos, smem, bias, trash, xstride, threadIdx.x & 7);
+      // waves without a unit skip the store (their trash writes would all
+      // hit the same LDS banks)
+      if (__any(ok)) piece_store(v, ok, pos, smem, bias, trash, xstride, threadIdx.x & 7);
       if constexpr (STAGE) {
         if (wb0 == 0) {
 #pragma unroll

@@ -118,8 +118,21 @@ __device__ __forceinline__ void tq1_store_unit(const Tq1Unit& un, unsigned char*
   const int kb = (((160 * (u0 + un.u)) >> 8) + 1) << 8;  // first block boundary of the span
   const int lim = kb - k0;
   unsigned char* dst = un.ok ? xs + un.m * xstride + un.u * kSpanBytes + g * kUnitBytes : trash;
+  // Activation i of the unit is kept in the masked copy when i >= lim: bit i
+  // of keep (all ones for lim <= 0, none for lim >= 40).
+  const uint64_t keep = lim <= 0 ? ~uint64_t{0} : (lim >= 40 ? uint64_t{0} : ~uint64_t{0} << lim);
+  const uint32_t keep_lo = (uint32_t)keep, keep_hi = (uint32_t)(keep >> 32);
+  // Running sum of the activations in order; the masked sum is the total
+  // minus the sum below lim (lim is a multiple of 8 when 0 < lim < 40: block
+  // boundaries sit 32, 64, 96 or 128 weights into a span).
   const half2v ones = {(_Float16)1.0f, (_Float16)1.0f};
-  float sa = 0.f, sb = 0.f;
+  float sa = 0.f, below = 0.f;
+#pragma unroll
+  for (int p = 0; p < 20; ++p) {
+    sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, e[p]), ones, sa, false);
+    if (p % 4 == 3) below = 2 * (p + 1) == lim ? sa : below;
+  }
+  float sb = lim <= 0 ? sa : (lim >= 40 ? 0.f : sa - below);
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
     u32x4 plain, masked;
@@ -130,12 +143,10 @@ __device__ __forceinline__ void tq1_store_unit(const Tq1Unit& un, unsigned char*
       const int b = 5 * kByteOfSlot[2 * t + 1] + j;
       const uint32_t sel = ((b & 1) ? 0x07060000u : 0x05040000u) | ((a & 1) ? 0x0302u : 0x0100u);
       plain[t] = perm(e[b >> 1], e[a >> 1], sel);
-      const uint32_t keep = (a >= lim ? 0x0000FFFFu : 0u) | (b >= lim ? 0xFFFF0000u : 0u);
-      masked[t] = plain[t] & keep;
-      // (a bit cast of a vector element itself reads element 0: copy first)
-      const uint32_t pv = plain[t], mv = masked[t];
-      sa = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, pv), ones, sa, false);
-      sb = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, mv), ones, sb, false);
+      // 0 or all ones from bit a / bit b of keep, merged into a half-word mask
+      const uint32_t ka = (uint32_t)__builtin_amdgcn_sbfe(a < 32 ? keep_lo : keep_hi, a & 31, 1);
+      const uint32_t kbm = (uint32_t)__builtin_amdgcn_sbfe(b < 32 ? keep_lo : keep_hi, b & 31, 1);
+      masked[t] = plain[t] & ((ka & 0x0000FFFFu) | (kbm & 0xFFFF0000u));
     }
     *reinterpret_cast<u32x4*>(dst + 16 * j) = plain;
     *reinterpret_cast<u32x4*>(dst + 16 * (5 + j)) = masked;
@@ -285,7 +296,9 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     auto span = [&](int i) { return cnt > 0 ? u0 + wk + WK * (i < cnt ? i : cnt - 1) : u0; };
     sfor1<0, D>([&](auto dd) { load(decltype(dd)::value, span(decltype(dd)::value)); });
     __syncthreads();  // the previous window is consumed
-    tq1_store_unit(un, smem, sums, trash, u0, q & 3, xstride, K);
+    // waves without a unit skip the store (their trash writes would all hit
+    // the same LDS banks)
+    if (__any(un.ok)) tq1_store_unit(un, smem, sums, trash, u0, q & 3, xstride, K);
     if constexpr (STAGE) {
       if (u0 == 0) {
 #pragma unroll
