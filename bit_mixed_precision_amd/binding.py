@@ -56,6 +56,7 @@ SIGNATURES = {
     "tq_gemm_tq2_ex": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "tq_gemm_tq1_ex": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _P]),
     "tq_gemm_tq2_tiled": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
+    "tq_gemm_tq2_tile": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P]),
     "tq_gemm_tq1_tiled": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_pack_dev_workspace_bytes": (_I64, [_I64, _I64]),
     "tq_pack_tq2_dev": (_I, [_P, _I64, _I64, C.c_double, _P, _P, _P, _P, _P, _I64, _P]),
@@ -218,6 +219,16 @@ def tq_gemm_tq2_tiled(X, qs, scales, mt: int, ng: int, kg: int, Y=None, stream=N
     Y = _out(Y, M, N, X)
     _check(lib.tq_gemm_tq2_tiled(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, ng, kg,
                                  _stream(stream)), "tq_gemm_tq2_tiled")
+    return Y
+
+
+def tq_gemm_tq2_tile(X, qs, scales, mt: int, nr: int, ng: int, kg: int, Y=None, stream=None):
+    """tq_gemm_tq2 on the tiled kernel with an explicit (mt, nr, ng, kg) tile."""
+    M, K = X.shape
+    N = qs.shape[0]
+    Y = _out(Y, M, N, X)
+    _check(lib.tq_gemm_tq2_tile(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, nr, ng, kg,
+                                _stream(stream)), "tq_gemm_tq2_tile")
     return Y
 
 

@@ -202,6 +202,19 @@ int tq_gemm_tq2_tiled(const void* X, const void* qs, const void* scales, void* Y
   return finish(tq::launch_tq2_tiled_shape(t, a, static_cast<hipStream_t>(stream)));
 }
 
+int tq_gemm_tq2_tile(const void* X, const void* qs, const void* scales, void* Y, int64_t M,
+                     int64_t N, int64_t K, int mt, int nr, int ng, int kg, void* stream) {
+  bool noop = false;
+  int st = check_gemm(X, qs, scales, Y, M, N, K, false, 0, &noop);
+  if (st != TQ_OK || noop) return st;
+  const tq::TiledShape t{mt, nr, ng, kg};
+  if (!tq::tiled_compiled(t)) return TQ_ERR_UNSUPPORTED;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  tq::GemmArgs a{X, qs, scales, Y, M, N, K, 0};
+  return finish(tq::launch_tq2_tiled_shape(t, a, static_cast<hipStream_t>(stream)));
+}
+
 int tq_gemm_tq1_tiled(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,
                       int64_t M, int64_t N, int64_t K, int mt, int nw, int kg, void* stream) {
   bool noop = false;

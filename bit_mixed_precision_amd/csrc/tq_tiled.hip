@@ -453,25 +453,34 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
 // half the activation re-reads) win once they alone fill about 85% of the
 // compute units: 128 x 128 (4 row groups of 32 x 2 k-groups: each decoded
 // weight feeds 8 MFMAs, the weights are read once) past M = 64, 64 x 128
-// (2 x 4) up to M = 64.  Below that the 4-wave tile of 1 row group x 4
-// k-groups (BN = 64, twice the workgroups), with 32 activation rows up to
-// M = 64 so that the activation-row tiles spread over more compute units.
+// (2 x 4) up to M = 64.  Below that 4-wave tiles of 1 row group x 4 k-groups,
+// 64 weight rows wide, with 32 activation rows up to M = 64 so that the
+// activation-row tiles spread over more compute units; 32 weight rows wide
+// when 64 would leave compute units idle (M <= 32: 18.4 against 23.1 us at
+// N = 8192); past M = 64 the 8-wave 64 x 64 tile (2 row groups of 32 x 4
+// k-groups: 32.0 against 34.6 us at N = 8192, M = 128).
 TiledShape tiled_shape(int64_t M, int64_t N) {
   const int64_t cus = device_cus();
+  auto fills = [&](const TiledShape& t) {
+    const int64_t bm = 16 * t.mt;
+    const int64_t bn = 16 * t.nr * t.ng;
+    const int64_t wgs = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+    return 20 * wgs >= 17 * cus;
+  };
   if (M > 32) {
     const bool wide = M > 64;
     const TiledShape t8 = wide ? TiledShape{8, 2, 4, 2} : TiledShape{4, 4, 2, 4};
-    const int64_t bm = 16 * t8.mt;
-    const int64_t bn = 16 * t8.nr * t8.ng;
-    const int64_t wgs = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
-    if (20 * wgs >= 17 * cus) return t8;
-    return wide ? TiledShape{4, 4, 1, 4} : TiledShape{2, 4, 1, 4};
+    if (fills(t8)) return t8;
+    return wide ? TiledShape{4, 2, 2, 4} : TiledShape{2, 4, 1, 4};
   }
-  return TiledShape{2, 4, 1, 4};
+  const TiledShape t{2, 4, 1, 4};
+  return fills(t) ? t : TiledShape{2, 2, 1, 4};
 }
 
 template <int MT>
 hipError_t launch_mt(const TiledShape& t, const GemmArgs& a, hipStream_t stream) {
+  if (t.nr == 2) return t.ng == 2 ? launch_tiled<MT, 2, 2, 4>(a, stream)
+                                  : launch_tiled<MT, 2, 1, 4>(a, stream);
   if (t.ng == 4) return launch_tiled<MT, 4, 4, 2>(a, stream);
   if (t.kg == 4) return t.ng == 2 ? launch_tiled<MT, 4, 2, 4>(a, stream)
                                   : launch_tiled<MT, 4, 1, 4>(a, stream);
@@ -480,7 +489,9 @@ hipError_t launch_mt(const TiledShape& t, const GemmArgs& a, hipStream_t stream)
 
 bool tiled_compiled(const TiledShape& t) {
   if (t.mt == 8) return t.nr == 2 && t.ng == 4 && t.kg == 2;
-  if ((t.mt != 2 && t.mt != 4) || t.nr != 4) return false;
+  if (t.mt != 2 && t.mt != 4) return false;
+  if (t.nr == 2) return t.kg == 4 && (t.ng == 1 || t.ng == 2);
+  if (t.nr != 4) return false;
   return (t.ng == 4 && t.kg == 2) || (t.ng == 2 && t.kg == 4) || (t.ng == 2 && t.kg == 2) ||
          (t.ng == 1 && t.kg == 4);
 }

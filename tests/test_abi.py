@@ -91,6 +91,19 @@ def test_tiled_tile_errors():
     assert _gt(3, 2, 2, X=None, M=0) == tq.TQ_OK
 
 
+def _gt4(mt, nr, ng, kg, X=A, M=40, K=512):
+    return tq.raw_call("tq_gemm_tq2_tile", X, A, A, A, M, 64, K, mt, nr, ng, kg, None)
+
+
+def test_tile_errors():
+    assert _gt4(2, 2, 1, 4, X=None) == tq.TQ_ERR_NULL
+    assert _gt4(2, 2, 1, 4, K=300) == tq.TQ_ERR_SHAPE
+    for tile in [(2, 2, 4, 2), (2, 2, 2, 2), (2, 3, 1, 4), (8, 4, 4, 2), (4, 1, 1, 4),
+                 (3, 2, 1, 4), (2, 2, 1, 8)]:
+        assert _gt4(*tile) == tq.TQ_ERR_UNSUPPORTED, tile
+    assert _gt4(3, 2, 1, 4, X=None, M=0) == tq.TQ_OK
+
+
 def _gt1(mt, nw, kg, X=A, M=40, K=512, ldq=112):
     return tq.raw_call("tq_gemm_tq1_tiled", X, A, ldq, A, A, M, 64, K, mt, nw, kg, None)
 

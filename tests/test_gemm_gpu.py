@@ -103,26 +103,33 @@ def test_small_parity(fmt, path, M, N, K):
     check_close(Y, ref(X, T, s), f"{fmt}/{path}/{M}x{N}x{K}")
 
 
-TILES = [(mt, ng, kg) for mt in (2, 4) for ng, kg in ((4, 2), (2, 4), (2, 2), (1, 4))]
-TILES.append((8, 4, 2))  # 128 activation rows x 32 weight rows per wave
+TILES = [(mt, 4, ng, kg) for mt in (2, 4) for ng, kg in ((4, 2), (2, 4), (2, 2), (1, 4))]
+TILES += [(mt, 2, ng, 4) for mt in (2, 4) for ng in (1, 2)]  # 32 weight rows per wave
+TILES.append((8, 2, 4, 2))  # 128 activation rows x 32 weight rows per wave
 # ragged in M and N, K / 256 = 1, 2, 3, 5 (fewer blocks than k-groups, odd counts)
 TILE_SHAPES = [(17, 100, 256), (40, 300, 768), (64, 257, 1024), (100, 520, 1280),
                (130, 1000, 512)]
 
 
-@pytest.mark.parametrize("mt,ng,kg", TILES)
+@pytest.mark.parametrize("mt,nr,ng,kg", TILES)
 @pytest.mark.parametrize("M,N,K", TILE_SHAPES)
-def test_every_tiled_tile(mt, ng, kg, M, N, K):
+def test_every_tiled_tile(mt, nr, ng, kg, M, N, K):
     """Each compiled tile of the tiled kernel, not only the ones the shape
-    heuristic picks, over several tiles and ragged tails."""
-    say(f"[tile] mt={mt} ng={ng} kg={kg} M={M} N={N} K={K}")
+    heuristic picks, over several tiles and ragged tails (tiles with the
+    default weight rows per wave also through tq_gemm_tq2_tiled)."""
+    say(f"[tile] mt={mt} nr={nr} ng={ng} kg={kg} M={M} N={N} K={K}")
     T, s = iid_problem(N, K, 0.31, 5)
     X = activations(M, K, 5)
     Xd, qd, sd = dev(X), dev(pack("tq2", T)), dev(s)
     Y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
-    tq.tq_gemm_tq2_tiled(Xd, qd, sd, mt, ng, kg, Y)
+    tq.tq_gemm_tq2_tile(Xd, qd, sd, mt, nr, ng, kg, Y)
     torch.cuda.synchronize()
-    check_close(Y.cpu().numpy(), ref(X, T, s), f"tile {mt},{ng},{kg} {M}x{N}x{K}")
+    check_close(Y.cpu().numpy(), ref(X, T, s), f"tile {mt},{nr},{ng},{kg} {M}x{N}x{K}")
+    if nr == (2 if mt == 8 else 4):
+        Y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+        tq.tq_gemm_tq2_tiled(Xd, qd, sd, mt, ng, kg, Y)
+        torch.cuda.synchronize()
+        check_close(Y.cpu().numpy(), ref(X, T, s), f"tiled {mt},{ng},{kg} {M}x{N}x{K}")
 
 
 TQ1_TILES = [(1, 4, 4), (2, 4, 2), (2, 4, 4), (4, 4, 1), (4, 4, 2), (2, 8, 2)]
