@@ -20,4 +20,6 @@ from .tq_oracle import (  # noqa: F401
     dequantize_ref,
     gemm_ref,
     gemm_bruteforce_ref,
+    silu_ref,
+    swiglu_ref,
 )

@@ -264,3 +264,19 @@ def gemm_bruteforce_ref(X, T, scales) -> np.ndarray:
             Y[m, n] = math.fsum(float(X[m, k]) * float(s[n, k // BLOCK]) * int(T[n, k])
                                 for k in range(K))
     return Y
+
+
+def silu_ref(g) -> np.ndarray:
+    """silu(g) = g / (1 + exp(-g)) in fp64 (the gate of the SwiGLU MLP the
+    project page's architecture section names)."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_ref(X, T_gate, s_gate, T_up, s_up, cols=None) -> np.ndarray:
+    """silu(X (s_g . T_g)^T) * (X (s_u . T_u)^T) in fp64: the gated MLP input
+    of the decode step, both products as gemm_ref."""
+    g = gemm_ref(X, T_gate, s_gate, cols)
+    u = gemm_ref(X, T_up, s_up, cols)
+    return silu_ref(g) * u

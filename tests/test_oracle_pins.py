@@ -321,3 +321,44 @@ def test_dequantize_block_index():
     s = np.array([[1.0, 2.0, 4.0]], np.float16)
     Wd = dequantize_ref(T, s)
     assert Wd[0, 255] == 1 and Wd[0, 256] == 2 and Wd[0, 511] == 2 and Wd[0, 512] == 4
+
+
+# ---- SwiGLU of the decode step (gated MLP named in the architecture section)
+
+def test_silu_closed_forms():
+    """silu(0) = 0; silu(ln 3) = (3/4) ln 3 (sigmoid(ln 3) = 3/4); the odd
+    identity silu(-x) = silu(x) - x; silu(x) -> x and -> 0 at the ends."""
+    from oracle import silu_ref
+    assert silu_ref(0.0) == 0.0
+    assert abs(silu_ref(math.log(3.0)) - 0.75 * math.log(3.0)) < 1e-15
+    x = np.linspace(-30, 30, 121)
+    assert np.allclose(silu_ref(-x), silu_ref(x) - x, rtol=0, atol=1e-13)
+    assert silu_ref(800.0) == 800.0 and silu_ref(-800.0) == 0.0
+    for v in (-7.5, -1.0, 0.25, 2.0, 9.0):
+        assert abs(silu_ref(v) - v / (1.0 + math.exp(-v))) <= 1e-15 * max(1.0, abs(v))
+
+
+def test_swiglu_composition():
+    """Identity gate: g = x exactly, so the result is silu(x) * u; zero up
+    matrix: exactly zero; brute force on a tiny random case."""
+    from oracle import swiglu_ref, silu_ref
+    rng = np.random.default_rng(17)
+    K = 256
+    X = rng.standard_normal((3, K)).astype(np.float16)
+    I = np.eye(K, dtype=np.int8)
+    one = np.ones((K, 1), np.float16)
+    Tu = rng.integers(-1, 2, (K, K)).astype(np.int8)
+    su = rng.uniform(0.5, 2, (K, 1)).astype(np.float16)
+    y = swiglu_ref(X, I, one, Tu, su)
+    u = gemm_ref(X, Tu, su)
+    assert np.array_equal(y, silu_ref(X.astype(np.float64)) * u)
+    assert not swiglu_ref(X, I, one, np.zeros((K, K), np.int8), one).any()
+    N = 4
+    Tg = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    sg = rng.uniform(0.01, 0.1, (N, 1)).astype(np.float16)
+    y = swiglu_ref(X, Tg, sg, Tu[:N], su[:N])
+    for m in range(3):
+        for n in range(N):
+            g = math.fsum(float(X[m, k]) * float(sg[n, 0]) * int(Tg[n, k]) for k in range(K))
+            uu = math.fsum(float(X[m, k]) * float(su[n, 0]) * int(Tu[n, k]) for k in range(K))
+            assert abs(y[m, n] - g / (1 + math.exp(-g)) * uu) <= 1e-12 * max(1.0, abs(y[m, n]))
