@@ -13,7 +13,8 @@ def __getattr__(name):
     import importlib
     if name.startswith("__"):
         raise AttributeError(name)
+    if name in ("binding", "build_lib"):
+        # submodules: resolving build_lib must not load the library it rebuilds
+        return importlib.import_module(__name__ + "." + name)
     binding = importlib.import_module(__name__ + ".binding")
-    if name == "binding":
-        return binding
     return getattr(binding, name)

@@ -57,6 +57,7 @@ SIGNATURES = {
     "tq_gemm_tq1_ex": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _P]),
     "tq_gemm_tq2_tiled": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_gemm_tq2_tile": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P]),
+    "tq_gemm_tq2_swiglu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_gemm_tq1_tiled": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_pack_dev_workspace_bytes": (_I64, [_I64, _I64]),
     "tq_pack_tq2_dev": (_I, [_P, _I64, _I64, C.c_double, _P, _P, _P, _P, _P, _I64, _P]),
@@ -219,6 +220,17 @@ def tq_gemm_tq2_tiled(X, qs, scales, mt: int, ng: int, kg: int, Y=None, stream=N
     Y = _out(Y, M, N, X)
     _check(lib.tq_gemm_tq2_tiled(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, ng, kg,
                                  _stream(stream)), "tq_gemm_tq2_tiled")
+    return Y
+
+
+def tq_gemm_tq2_swiglu(X, qs_gate, scales_gate, qs_up, scales_up, Y=None, stream=None):
+    """silu(X G^T) * (X U^T) for TQ2 gate / up matrices, M <= 16, one launch."""
+    M, K = X.shape
+    N = qs_gate.shape[0]
+    Y = _out(Y, M, N, X)
+    _check(lib.tq_gemm_tq2_swiglu(_ptr(X), _ptr(qs_gate), _ptr(scales_gate), _ptr(qs_up),
+                                  _ptr(scales_up), _ptr(Y), M, N, K, _stream(stream)),
+           "tq_gemm_tq2_swiglu")
     return Y
 
 

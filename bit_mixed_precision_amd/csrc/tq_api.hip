@@ -202,6 +202,21 @@ int tq_gemm_tq2_tiled(const void* X, const void* qs, const void* scales, void* Y
   return finish(tq::launch_tq2_tiled_shape(t, a, static_cast<hipStream_t>(stream)));
 }
 
+int tq_gemm_tq2_swiglu(const void* X, const void* qs_gate, const void* scales_gate,
+                       const void* qs_up, const void* scales_up, void* Y, int64_t M, int64_t N,
+                       int64_t K, void* stream) {
+  bool noop = false;
+  int st = check_gemm(X, qs_gate, scales_gate, Y, M, N, K, false, 0, &noop);
+  if (st != TQ_OK || noop) return st;
+  if (!qs_up || !scales_up) return TQ_ERR_NULL;
+  if (!aligned16(qs_up) || !aligned16(scales_up)) return TQ_ERR_ALIGN;
+  if (M > kSkinnyMaxM) return TQ_ERR_UNSUPPORTED;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  tq::GemmArgs a{X, qs_gate, scales_gate, Y, M, N, K, 0};
+  return finish(tq::launch_tq2_swiglu(a, qs_up, scales_up, static_cast<hipStream_t>(stream)));
+}
+
 int tq_gemm_tq2_tile(const void* X, const void* qs, const void* scales, void* Y, int64_t M,
                      int64_t N, int64_t K, int mt, int nr, int ng, int kg, void* stream) {
   bool noop = false;

@@ -29,6 +29,11 @@ int skinny_rows(int64_t N);
 int skinny_depth();                      // register ring depth (template argument)
 int skinny_stage(int64_t N, int64_t K, int64_t M);  // 1 when block scales are staged in LDS
 hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream);
+// Fused decode-step gate / up product: a.qs / a.scales the gate matrix, Y =
+// silu(X G^T) * (X U^T), M <= 16.
+hipError_t launch_tq2_swiglu(const GemmArgs& a, const void* qs_up, const void* scales_up,
+                             hipStream_t stream);
+int glu_rows(int64_t N);
 
 // TQ1 MFMA kernel: any M, in slices of 16 activation rows.
 hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream);

@@ -162,10 +162,16 @@ __device__ __forceinline__ void piece_store(const u32x4 (&v)[4], bool ok, PieceP
 // workgroup's rows are copied to LDS as fp32 (else each block's scale comes
 // with its weights).  Rows past N and activation rows past M read valid dummy
 // data whose results are never written (MFMA rows and columns do not mix).
-template <int D, bool STAGE>
+//
+// GLU: the workgroup's first RG / 2 row groups read the gate matrix (qs,
+// scales), the others the same rows of the up matrix (qs2, scales2), and the
+// output is silu(g) u of the two products (SwiGLU of the decode step), one
+// fp16 rounding.
+template <int D, bool STAGE, bool GLU>
 __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ qs,
-    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int M, int N, int K, int RG,
+    const uint16_t* __restrict__ scales, const uint8_t* __restrict__ qs2,
+    const uint16_t* __restrict__ scales2, uint16_t* __restrict__ Y, int M, int N, int K, int RG,
     int lwk, int nbw, int xregion) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -178,23 +184,30 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   const int T = 64 * W;        // threads
   const int rg = wave >> lwk;  // row group of this wave
   const int wk = wave & (WK - 1);  // K slice of this wave
-  const int n_base = blockIdx.x * (16 * RG);
-  const int rows = min(16 * RG, N - n_base);
+  const int RGO = GLU ? RG >> 1 : RG;  // output row groups
+  const bool up = GLU && rg >= RGO;    // wave-uniform: this wave reads the up matrix
+  const int rgo = up ? rg - RGO : rg;
+  const int n_base = blockIdx.x * (16 * RGO);
+  const int rows = min(16 * RGO, N - n_base);
   const int xstride = nbw * 512 + kXRowPad;
   const size_t row_bytes = (size_t)(K >> 2);
   float* bias = reinterpret_cast<float*>(smem + M * xstride);
   unsigned char* trash = reinterpret_cast<unsigned char*>(bias + 16 * nbw);
   float* sc_lds = reinterpret_cast<float*>(smem + xregion);
 
-  const int nrow = 16 * rg + li < rows ? 16 * rg + li : 0;  // row of this lane in the tile
-  const uint8_t* wrow = qs + (size_t)(n_base + nrow) * row_bytes + 16 * g;
-  const uint16_t* srow = scales + (size_t)(n_base + nrow) * nb;
+  const int nrow = 16 * rgo + li < rows ? 16 * rgo + li : 0;  // row of this lane in the tile
+  const uint8_t* wrow = (up ? qs2 : qs) + (size_t)(n_base + nrow) * row_bytes + 16 * g;
+  const uint16_t* srow = (up ? scales2 : scales) + (size_t)(n_base + nrow) * nb;
   const unsigned char* xa = smem + (li < M ? li : M - 1) * xstride + g * 128;
   const float* ba = bias + 4 * g;
 
-  // The workgroup's block scales (staged with the first window).
+  // The workgroup's block scales (staged with the first window): ns of each
+  // matrix, the up matrix's after the gate matrix's.
   const int ns = STAGE ? rows * nb : 0;
+  const int ns_all = GLU ? 2 * ns : ns;
   const uint16_t* ssrc = scales + (size_t)n_base * nb;
+  const uint16_t* ssrc2 = GLU ? scales2 + (size_t)n_base * nb : ssrc;
+  const int sc_off = up ? ns : 0;
 
   float4v acc = {0.f, 0.f, 0.f, 0.f};
   u32x4 wbuf[D];
@@ -208,7 +221,7 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   auto compute = [&](int d, int b, int bw) {
     const u32x4 w = wbuf[d];
     const u32x4 w8 = shift8(w);
-    const float sc = STAGE ? sc_lds[nrow * nb + b] : h2f(sbuf[d]);
+    const float sc = STAGE ? sc_lds[sc_off + nrow * nb + b] : h2f(sbuf[d]);
     float4v c0 = *reinterpret_cast<const float4v*>(ba + 16 * bw);  // -2^-24 (row sums)
     float4v c1 = {0.f, 0.f, 0.f, 0.f};
     const unsigned char* xb = xa + bw * 512;
@@ -267,9 +280,9 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
 #pragma unroll
         for (int r = 0; r < kScaleRegs; ++r) {
           int e = threadIdx.x + r * T;
-          e = e < ns ? e : 0;
+          e = e < ns_all ? e : 0;
           asm volatile("" : "+v"(e));  // keep the load in the window (not hoisted ahead of it)
-          sreg[r] = ssrc[e];
+          sreg[r] = e < ns ? ssrc[e] : ssrc2[e - ns];
         }
       }
       static_for<0, D>([&](auto dd) { load(decltype(dd)::value, blk(decltype(dd)::value)); });
@@ -281,7 +294,7 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
 #pragma unroll
           for (int r = 0; r < kScaleRegs; ++r) {
             const int e = threadIdx.x + r * T;
-            if (e < ns) sc_lds[e] = h2f(sreg[r]);
+            if (e < ns_all) sc_lds[e] = h2f(sreg[r]);
           }
         }
       }
@@ -309,7 +322,7 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave * 256 + i * 64 + lane] = acc[i];
   __syncthreads();
-  for (int t = threadIdx.x; t < RG * 256; t += T) {
+  for (int t = threadIdx.x; t < RGO * 256; t += T) {
     const int r = t >> 8;
     const int e = t & 255;
     const int l = e & 63;
@@ -318,7 +331,13 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
     if (m < M && n < rows) {
       float sum = 0.f;
       for (int k = 0; k < WK; ++k) sum += red[(r * WK + k) * 256 + e];
-      Y[(size_t)m * N + n_base + n] = f2h_bits(sum * 0x1p24f);
+      sum *= 0x1p24f;
+      if constexpr (GLU) {
+        float u = 0.f;
+        for (int k = 0; k < WK; ++k) u += red[((RGO + r) * WK + k) * 256 + e];
+        sum = sum / (1.0f + expf(-sum)) * (u * 0x1p24f);  // silu(g) u
+      }
+      Y[(size_t)m * N + n_base + n] = f2h_bits(sum);
     }
   }
 }
@@ -335,21 +354,23 @@ int pick_rows(int64_t N, int cus) {
 
 constexpr int kDepth = 4;
 
-template <bool STAGE>
-hipError_t launch_tq2_skinny_s(const GemmArgs& a, hipStream_t stream, int RG, int lwk, int nbw,
-                               int xregion, int lds) {
+template <bool STAGE, bool GLU>
+hipError_t launch_tq2_skinny_s(const GemmArgs& a, const void* qs2, const void* scales2,
+                               hipStream_t stream, int RG, int lwk, int nbw, int xregion, int lds) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(tq2_skinny_kernel<kDepth, STAGE>),
+        reinterpret_cast<const void*>(tq2_skinny_kernel<kDepth, STAGE, GLU>),
         hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t groups = (a.N + 16 * RG - 1) / (16 * RG);
-  hipLaunchKernelGGL((tq2_skinny_kernel<kDepth, STAGE>), dim3((unsigned)groups),
+  const int RGO = GLU ? RG / 2 : RG;
+  const int64_t groups = (a.N + 16 * RGO - 1) / (16 * RGO);
+  hipLaunchKernelGGL((tq2_skinny_kernel<kDepth, STAGE, GLU>), dim3((unsigned)groups),
                      dim3(64 * (RG << lwk)), lds, stream, static_cast<const uint16_t*>(a.X),
                      static_cast<const uint8_t*>(a.qs), static_cast<const uint16_t*>(a.scales),
+                     static_cast<const uint8_t*>(qs2), static_cast<const uint16_t*>(scales2),
                      static_cast<uint16_t*>(a.Y), (int)a.M, (int)a.N, (int)a.K, RG, lwk, nbw,
                      xregion);
   return hipGetLastError();
@@ -387,10 +408,12 @@ int skinny_lwk(int64_t N, int64_t K, int64_t M) {
   return lwk;
 }
 
-hipError_t launch_tq2_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk) {
+// Common launch: RG row groups in all (two matrices of RG / 2 each when
+// glu), 2^lwk waves per row group.
+hipError_t launch_skinny_rg(const GemmArgs& a, const void* qs2, const void* scales2, bool glu,
+                            hipStream_t stream, int RG, int lwk) {
   const int M = (int)a.M, K = (int)a.K;
   const int nb = K / 256;
-  const int RG = skinny_rows(a.N);
   const int W = RG << lwk;
   if (lwk < 0 || W > 16) return hipErrorInvalidValue;
   // activation window: as many blocks as fit the LDS budget with their sums
@@ -405,12 +428,41 @@ hipError_t launch_tq2_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk)
   const bool stage = sbytes <= kScaleLdsMax && int64_t{16} * RG * nb <= int64_t{kScaleRegs} * 64 * W;
   const int lds = xregion + (stage ? (int)sbytes : 0);
   if (lds > kLdsLimit) return hipErrorInvalidValue;
-  return stage ? launch_tq2_skinny_s<true>(a, stream, RG, lwk, nbw, xregion, lds)
-               : launch_tq2_skinny_s<false>(a, stream, RG, lwk, nbw, xregion, lds);
+  if (glu)
+    return stage ? launch_tq2_skinny_s<true, true>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds)
+                 : launch_tq2_skinny_s<false, true>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds);
+  return stage ? launch_tq2_skinny_s<true, false>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds)
+               : launch_tq2_skinny_s<false, false>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds);
+}
+
+hipError_t launch_tq2_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk) {
+  return launch_skinny_rg(a, nullptr, nullptr, false, stream, skinny_rows(a.N), lwk);
 }
 
 hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream) {
   return launch_tq2_skinny_lwk(a, stream, skinny_lwk(a.N, a.K, a.M));
+}
+
+// Waves per row group for the fused gate / up product: the same rule as
+// skinny_lwk for 2 RGO row groups.
+int glu_rows(int64_t N) {
+  const int r = skinny_rows(N);
+  return r > 8 ? 8 : r;
+}
+
+int glu_lwk(int64_t N, int64_t K, int64_t M) {
+  const int RG = 2 * glu_rows(N);
+  const int64_t nb = K / 256;
+  const int64_t min_blocks = M <= 2 ? 8 : 1;
+  int lwk = 0;
+  while ((RG << (lwk + 1)) <= 16 && (min_blocks << (lwk + 1)) <= nb) ++lwk;
+  return lwk;
+}
+
+hipError_t launch_tq2_swiglu(const GemmArgs& a, const void* qs_up, const void* scales_up,
+                             hipStream_t stream) {
+  return launch_skinny_rg(a, qs_up, scales_up, true, stream, 2 * glu_rows(a.N),
+                          glu_lwk(a.N, a.K, a.M));
 }
 
 }  // namespace tq

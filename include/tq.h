@@ -190,6 +190,22 @@ int tq_pack_tq1_dev(const float* W, int64_t N, int64_t K, double eps, int64_t ld
 int tq_gemm_tq2_tiled(const void* X, const void* qs, const void* scales_f16, void* Y,
                       int64_t M, int64_t N, int64_t K, int mt, int ng, int kg, void* stream);
 
+/* Fused gate / up product of the decode step's gated MLP (SwiGLU, named in
+ * the architecture section of the project page "Scaling Laws and Efficient
+ * Inference for Ternary Language Models"; each product as in "The model"):
+ *   Y[m][n] = silu(g) * u,  g = sum_k X[m][k] s_g[n][k/256] T_g[n][k],
+ *                           u = sum_k X[m][k] s_u[n][k/256] T_u[n][k],
+ * silu(g) = g / (1 + exp(-g)), g, u and the product in fp32, one fp16
+ * rounding.  Gate and up matrices are TQ2 packed as for tq_gemm_tq2 (qs
+ * [N][K/4], scales [N][K/256] fp16), both N x K; X [M][K] and Y [M][N] fp16,
+ * all device pointers, 16-byte aligned, owned by the caller.  For decode
+ * sizes: 1 <= M <= 16 (larger M gives TQ_ERR_UNSUPPORTED); one launch streams
+ * both matrices, the skinny kernel's offset rounding applies to g and u.
+ * Errors as tq_gemm_tq2 (M = 0 or N = 0 is a no-op returning TQ_OK). */
+int tq_gemm_tq2_swiglu(const void* X, const void* qs_gate, const void* scales_gate_f16,
+                       const void* qs_up, const void* scales_up_f16, void* Y, int64_t M,
+                       int64_t N, int64_t K, void* stream);
+
 /* As tq_gemm_tq2_tiled with the weight rows per wave explicit: 16 mt
  * activation rows x 16 nr ng weight rows per workgroup of ng x kg waves.
  * Compiled tiles (mt, nr, ng, kg): mt in {2, 4} with (4, 4, 2), (4, 2, 4),

@@ -5,6 +5,7 @@ import ctypes as C
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -183,3 +184,32 @@ def test_one_hip_runtime_per_process():
     out = subprocess.run(["python", "-c", code], cwd=ROOT, capture_output=True, text=True,
                          check=True).stdout.split()
     assert out == ["1", "1"], out
+
+
+def _sg(X=A, gate=A, up=A, M=4, N=64, K=512, Y=A):
+    return tq.raw_call("tq_gemm_tq2_swiglu", X, gate, A, up, A, Y, M, N, K, None)
+
+
+def test_swiglu_argument_errors():
+    """Checks in order: shape of M, N, then null, shape of K, alignment, then
+    the decode-size limit (M <= 16), all before any device work."""
+    assert _sg(M=0, X=None) == tq.TQ_OK
+    assert _sg(N=0, up=None) == tq.TQ_OK
+    assert _sg(M=-1) == tq.TQ_ERR_SHAPE
+    assert _sg(X=None) == tq.TQ_ERR_NULL
+    assert _sg(gate=None) == tq.TQ_ERR_NULL
+    assert _sg(up=None) == tq.TQ_ERR_NULL
+    assert _sg(K=300) == tq.TQ_ERR_SHAPE
+    assert _sg(up=A + 2) == tq.TQ_ERR_ALIGN
+    assert _sg(M=17) == tq.TQ_ERR_UNSUPPORTED
+
+
+def test_build_step_does_not_load_the_library():
+    """Resolving the build module must not load libtq.so (a library loaded
+    before a rebuild stays mapped, and the fresh symbols would be missing)."""
+    code = ("import sys; sys.path.insert(0, %r); "
+            "from bit_mixed_precision_amd import build_lib; "
+            "import bit_mixed_precision_amd.build_lib; "
+            "print('bit_mixed_precision_amd.binding' in sys.modules)") % ROOT
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
+    assert out.stdout.strip() == "False"

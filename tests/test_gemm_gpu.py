@@ -356,6 +356,69 @@ def test_prefill_sizes(fmt, M, N):
     check_close(Y[:, cols], ref(X, T, s, cols=cols), f"prefill {fmt} M={M} N={N}")
 
 
+# ---- fused decode-step linears
+
+SWIGLU_SHAPES = [(1, 100, 256), (5, 300, 768), (16, 1000, 2048), (3, 4096, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", SWIGLU_SHAPES)
+def test_swiglu_parity(M, N, K):
+    """Fused gate / up + SwiGLU against the fp64 oracle: ragged N, one to
+    several row groups per workgroup, K with 1..32 blocks."""
+    from oracle import swiglu_ref
+    say(f"[swiglu] M={M} N={N} K={K}")
+    Tg, sg = iid_problem(N, K, 0.31, 41)
+    Tu, su = iid_problem(N, K, 0.31, 42)
+    X = activations(M, K, 43)
+    Y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    tq.tq_gemm_tq2_swiglu(dev(X), dev(pack("tq2", Tg)), dev(sg), dev(pack("tq2", Tu)), dev(su), Y)
+    torch.cuda.synchronize()
+    check_close(Y.cpu().numpy(), swiglu_ref(X, Tg, sg, Tu, su), f"swiglu {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_swiglu_layer_shape(M):
+    """The 70B gate / up shape (K = 8192, N = 28672) on 256 sampled columns
+    (first and last included), every output finite."""
+    from oracle import swiglu_ref
+    K, N = 8192, 28672
+    say(f"[swiglu] layer M={M}")
+    Tg, sg = iid_problem(N, K, 0.31, 44)
+    Tu, su = iid_problem(N, K, 0.31, 45)
+    X = activations(M, K, 46)
+    Y = tq.tq_gemm_tq2_swiglu(dev(X), dev(pack("tq2", Tg)), dev(sg), dev(pack("tq2", Tu)),
+                              dev(su)).cpu().numpy()
+    assert np.all(np.isfinite(Y.astype(np.float32)))
+    cols = np.sort(seed_for(47, N).choice(N, 256, replace=False))
+    cols[0], cols[-1] = 0, N - 1
+    check_close(Y[:, cols], swiglu_ref(X, Tg, sg, Tu, su, cols=cols), f"swiglu layer M={M}")
+
+
+def test_qkv_as_one_product():
+    """q, k and v of a layer as one product over the row-concatenated packed
+    matrices (N = 8192 + 1024 + 1024): one launch, and each slice of Y equals
+    its own product against the oracle."""
+    K = 8192
+    parts = [(8192, 51), (1024, 52), (1024, 53)]
+    Ts = [iid_problem(n, K, 0.31, sd) for n, sd in parts]
+    T = np.concatenate([t for t, _ in Ts])
+    s = np.concatenate([sc for _, sc in Ts])
+    qs = pack("tq2", T)
+    assert np.array_equal(qs, np.concatenate([pack("tq2", t) for t, _ in Ts]))
+    for M in (1, 4):
+        say(f"[qkv] M={M}")
+        X = activations(M, K, 54 + M)
+        Y = run("tq2", X, qs, s, "auto").cpu().numpy()
+        cols = np.sort(seed_for(55, M).choice(T.shape[0], 192, replace=False))
+        cols[0], cols[-1] = 0, T.shape[0] - 1
+        check_close(Y[:, cols], ref(X, T, s, cols=cols), f"qkv M={M}")
+        n0 = 0
+        for (t, sc), (n, _) in zip(Ts, parts):
+            c = np.array([0, n // 2, n - 1])
+            check_close(Y[:, n0 + c], ref(X, t, sc, cols=c), f"qkv slice {n} M={M}")
+            n0 += n
+
+
 def test_empty_is_noop():
     X = torch.empty((0, 256), dtype=torch.float16, device="cuda")
     q = torch.empty((16, 64), dtype=torch.uint8, device="cuda")
