@@ -365,7 +365,10 @@ STACK_MS = [1, 16]
 
 def stack_bench(args):
     """All 560 TQ2 linears of the stack, each with its own weights in HBM, back to
-    back in one HIP graph per M (activations random per linear shape)."""
+    back in one HIP graph per M (activations random per linear shape), run two
+    ways over the same buffers: seven products per layer, and the fused decode
+    step of four launches per layer (q, k, v as one product over the
+    row-concatenated matrices; o; gate / up with SwiGLU in one launch; down)."""
     import torch
     import bit_mixed_precision_amd.binding as tq
     from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
@@ -374,59 +377,92 @@ def stack_bench(args):
     torch.cuda.set_device(0)
     base = {}
     for name, K, N in STACK_LAYER:
-        if (K, N) in base:
-            continue
-        rng = seed_for(800, K, N)
+        rng = seed_for(800, K, N, len(name))
         T = ternary_iid(rng, N, K, 0.31)
         s = block_scales_fp16(rng, N, K)
-        base[(K, N)] = (torch.from_numpy(tq.tq_pack_tq2(T)[0]).cuda(), torch.from_numpy(s).cuda())
+        base[name] = (tq.tq_pack_tq2(T)[0], s)
         del T
-    weights = []  # every linear of every layer in its own buffers
+    qkv_q = np.concatenate([base[n][0] for n in ("q", "k", "v")])
+    qkv_s = np.concatenate([base[n][1] for n in ("q", "k", "v")])
+    dev = lambda a: torch.from_numpy(a).cuda()
+    layers = []  # every linear of every layer in its own buffers
     for _ in range(STACK_LAYERS):
-        weights.append([(name, K, N, base[(K, N)][0].clone(), base[(K, N)][1].clone())
-                        for name, K, N in STACK_LAYER])
+        L = {"qkv": (dev(qkv_q), dev(qkv_s))}
+        r0 = 0
+        for n in ("q", "k", "v"):
+            rows = base[n][0].shape[0]
+            L[n] = (L["qkv"][0][r0:r0 + rows], L["qkv"][1][r0:r0 + rows])  # views, same memory
+            r0 += rows
+        for n in ("o", "gate", "up", "down"):
+            L[n] = (dev(base[n][0]), dev(base[n][1]))
+        layers.append(L)
     torch.cuda.synchronize()
     log(f"[bench] stack: {STACK_LAYERS} layers x {len(STACK_LAYER)} linears in HBM")
+    dims = {name: (K, N) for name, K, N in STACK_LAYER}
     results = []
     stream = torch.cuda.current_stream()
     for M in STACK_MS:
         xs = {K: torch.from_numpy(activations_fp16(seed_for(801, M, K), M, K)).cuda()
-              for _, K, _ in STACK_LAYER}
-        ys = {N: torch.empty((M, N), dtype=torch.float16, device="cuda") for _, _, N in STACK_LAYER}
+              for K in (8192, 28672)}
+        ys = {N: torch.empty((M, N), dtype=torch.float16, device="cuda")
+              for N in (1024, 8192, 10240, 28672)}
 
-        def step(sp):
-            for layer in weights:
-                for name, K, N, q, sc in layer:
-                    st = tq.lib.tq_gemm_tq2(xs[K].data_ptr(), q.data_ptr(), sc.data_ptr(),
-                                            ys[N].data_ptr(), M, N, K, sp)
-                    if st != 0:
-                        raise RuntimeError(tq.tq_status_string(st))
+        def gemm(q, sc, K, N, sp):
+            st = tq.lib.tq_gemm_tq2(xs[K].data_ptr(), q.data_ptr(), sc.data_ptr(),
+                                    ys[N].data_ptr(), M, N, K, sp)
+            if st != 0:
+                raise RuntimeError(tq.tq_status_string(st))
 
-        step(stream.cuda_stream)  # eager pass: kernel attributes outside capture
-        torch.cuda.synchronize()
-        cap = torch.cuda.Stream()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                step(cap.cuda_stream)
-        for _ in range(2):
-            g.replay()
-        torch.cuda.synchronize()
-        reps = max(1, args.steps // 4)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
+        def step_separate(sp):
+            for L in layers:
+                for name, K, N in STACK_LAYER:
+                    gemm(*L[name], K, N, sp)
+
+        def step_fused(sp):
+            for L in layers:
+                gemm(*L["qkv"], 8192, 10240, sp)
+                gemm(*L["o"], 8192, 8192, sp)
+                st = tq.lib.tq_gemm_tq2_swiglu(xs[8192].data_ptr(), L["gate"][0].data_ptr(),
+                                               L["gate"][1].data_ptr(), L["up"][0].data_ptr(),
+                                               L["up"][1].data_ptr(), ys[28672].data_ptr(), M,
+                                               28672, 8192, sp)
+                if st != 0:
+                    raise RuntimeError(tq.tq_status_string(st))
+                gemm(*L["down"], 28672, 8192, sp)
+
+        row = {"M": M}
+        for label, step in (("separate", step_separate), ("fused", step_fused)):
+            step(stream.cuda_stream)  # eager pass: kernel attributes outside capture
+            torch.cuda.synchronize()
+            cap = torch.cuda.Stream()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    step(cap.cuda_stream)
+            for _ in range(2):
+                g.replay()
+            torch.cuda.synchronize()
+            reps = max(1, args.steps // 4)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            row[label + "_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+            del g
+        ms = min(row["separate_ms"], row["fused_ms"])
         nbytes = STACK_LAYERS * sum(alg_bytes("tq2", M, N, K) for _, K, N in STACK_LAYER)
         flops = STACK_LAYERS * sum(alg_flops(M, N, K) for _, K, N in STACK_LAYER)
         roof = max(nbytes / HBM_PEAK, flops / MFMA_F16_PEAK)
-        results.append({"M": M, "ms_per_step": round(ms, 4), "TBps": round(nbytes / ms / 1e9, 3),
-                        "roofline_ms": round(roof * 1e3, 4), "roof_frac": round(roof * 1e3 / ms, 4)})
-        log(f"[bench] stack M={M}: {ms:.3f} ms per step ({nbytes / ms / 1e9:.2f} TB/s)")
-        del g
+        row.update({"ms_per_step": row["fused_ms"], "TBps": round(nbytes / row["fused_ms"] / 1e9, 3),
+                    "roofline_ms": round(roof * 1e3, 4),
+                    "roof_frac": round(roof * 1e3 / row["fused_ms"], 4),
+                    "launches_per_step": {"separate": STACK_LAYERS * len(STACK_LAYER),
+                                          "fused": STACK_LAYERS * 4}})
+        results.append(row)
+        log(f"[bench] stack M={M}: separate {row['separate_ms']:.3f} ms, fused {row['fused_ms']:.3f} ms "
+            f"per step ({nbytes / ms / 1e9:.2f} TB/s at the better)")
     return results
 
 
@@ -477,14 +513,15 @@ def main():
         rows = stack_bench(args)
         m1 = rows[0]
         out = {
-            "metric": "80-layer ternary stack: 560 TQ2 GEMMs per step vs HBM roofline (M = 1, 16)",
+            "metric": "80-layer ternary stack: 560 TQ2 linears per step (fused: 320 launches) vs HBM roofline (M = 1, 16)",
             "value": m1["roof_frac"],
             "unit": "fraction of roofline at M = 1 (HBM 8 TB/s)",
             "n_gpus": 1, "steps": args.steps, "warmup": 2, "ms_per_step": m1["ms_per_step"],
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "f16", "data": "synthetic",
             "config": {"workload": "80 x {q 8192->8192, k/v 8192->1024, o 8192->8192, gate/up "
-                                   "8192->28672, down 28672->8192}, 17.65 GB TQ2, one HIP graph",
+                                   "8192->28672, down 28672->8192}, 17.65 GB TQ2, one HIP graph; "
+                                   "fused step: qkv as one product, gate/up + SwiGLU in one launch",
                        "global_batch": None, "seq_len": None, "parallelism": "none"},
             "per_M": rows,
         }
