@@ -22,4 +22,5 @@ from .tq_oracle import (  # noqa: F401
     gemm_bruteforce_ref,
     silu_ref,
     swiglu_ref,
+    gemm_bwd_x_ref,
 )

@@ -280,3 +280,14 @@ def swiglu_ref(X, T_gate, s_gate, T_up, s_up, cols=None) -> np.ndarray:
     g = gemm_ref(X, T_gate, s_gate, cols)
     u = gemm_ref(X, T_up, s_up, cols)
     return silu_ref(g) * u
+
+
+def gemm_bwd_x_ref(dY, T, scales) -> np.ndarray:
+    """dX = dY (s . T) in fp64: the input gradient of Y = X (s . T)^T (the
+    backward pass of quantization-aware training, "The model": the forward
+    uses the ternary weights, the backward the same product transposed)."""
+    dY64 = np.asarray(dY).astype(np.float64)
+    Wd = dequantize_ref(T, scales)
+    if dY64.shape[1] != Wd.shape[0]:
+        raise ValueError("dY and T disagree on N")
+    return dY64 @ Wd

@@ -362,3 +362,30 @@ def test_swiglu_composition():
             g = math.fsum(float(X[m, k]) * float(sg[n, 0]) * int(Tg[n, k]) for k in range(K))
             uu = math.fsum(float(X[m, k]) * float(su[n, 0]) * int(Tu[n, k]) for k in range(K))
             assert abs(y[m, n] - g / (1 + math.exp(-g)) * uu) <= 1e-12 * max(1.0, abs(y[m, n]))
+
+
+# ---- input gradient of the ternary product (QAT backward)
+
+def test_bwd_x_adjoint():
+    """<X (sT)^T, dY> = <X, dY (sT)> for any X, dY: the backward product is
+    the adjoint of gemm_ref (a transposed operand or a wrong scale index
+    breaks it); identity weights give dX = dY; fsum brute force on a tiny
+    case."""
+    from oracle import gemm_bwd_x_ref
+    rng = np.random.default_rng(23)
+    M, N, K = 5, 7, 512
+    T = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    s = rng.uniform(0.01, 0.1, (N, K // 256)).astype(np.float16)
+    X = rng.standard_normal((M, K))
+    dY = rng.standard_normal((M, N))
+    lhs = float(np.sum(gemm_ref(X, T, s) * dY))
+    rhs = float(np.sum(X * gemm_bwd_x_ref(dY, T, s)))
+    assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs))
+    I = np.eye(256, dtype=np.int8)
+    d = rng.standard_normal((3, 256)).astype(np.float16)
+    assert np.array_equal(gemm_bwd_x_ref(d, I, np.ones((256, 1), np.float16)), d.astype(np.float64))
+    G = gemm_bwd_x_ref(dY, T, s)
+    for m in range(M):
+        for k in (0, 255, 256, 511):
+            want = math.fsum(float(dY[m, n]) * float(s[n, k // 256]) * int(T[n, k]) for n in range(N))
+            assert abs(G[m, k] - want) <= 1e-12 * max(1.0, abs(want))
