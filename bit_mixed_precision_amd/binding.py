@@ -58,6 +58,7 @@ SIGNATURES = {
     "tq_gemm_tq2_tiled": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_gemm_tq2_tile": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P]),
     "tq_gemm_tq2_swiglu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "tq_gemm_tq2_bwd_x": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_gemm_tq1_tiled": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_pack_dev_workspace_bytes": (_I64, [_I64, _I64]),
     "tq_pack_tq2_dev": (_I, [_P, _I64, _I64, C.c_double, _P, _P, _P, _P, _P, _I64, _P]),
@@ -232,6 +233,16 @@ def tq_gemm_tq2_swiglu(X, qs_gate, scales_gate, qs_up, scales_up, Y=None, stream
                                   _ptr(scales_up), _ptr(Y), M, N, K, _stream(stream)),
            "tq_gemm_tq2_swiglu")
     return Y
+
+
+def tq_gemm_tq2_bwd_x(dY, qs, scales, dX=None, stream=None):
+    """dX = dY (s . T): the input gradient of tq_gemm_tq2 (N % 8 == 0)."""
+    M, N = dY.shape
+    K = qs.shape[1] * 4
+    dX = _out(dX, M, K, dY)
+    _check(lib.tq_gemm_tq2_bwd_x(_ptr(dY), _ptr(qs), _ptr(scales), _ptr(dX), M, N, K,
+                                 _stream(stream)), "tq_gemm_tq2_bwd_x")
+    return dX
 
 
 def tq_gemm_tq2_tile(X, qs, scales, mt: int, nr: int, ng: int, kg: int, Y=None, stream=None):

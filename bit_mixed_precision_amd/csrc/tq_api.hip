@@ -217,6 +217,19 @@ int tq_gemm_tq2_swiglu(const void* X, const void* qs_gate, const void* scales_ga
   return finish(tq::launch_tq2_swiglu(a, qs_up, scales_up, static_cast<hipStream_t>(stream)));
 }
 
+int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales, void* dX, int64_t M,
+                      int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N < 0) return TQ_ERR_SHAPE;
+  if (M == 0) return TQ_OK;
+  if (!dY || !qs || !scales || !dX) return TQ_ERR_NULL;
+  if (N == 0 || N % 8 || M > kMaxMN || N > kMaxMN || K < 256 || K % 256 || K > kMaxK)
+    return TQ_ERR_SHAPE;
+  if (!aligned16(dY) || !aligned16(qs) || !aligned16(scales) || !aligned16(dX)) return TQ_ERR_ALIGN;
+  int st = device_ready();
+  if (st != TQ_OK) return st;
+  return finish(tq::launch_tq2_bwd_x(dY, qs, scales, dX, M, N, K, static_cast<hipStream_t>(stream)));
+}
+
 int tq_gemm_tq2_tile(const void* X, const void* qs, const void* scales, void* Y, int64_t M,
                      int64_t N, int64_t K, int mt, int nr, int ng, int kg, void* stream) {
   bool noop = false;

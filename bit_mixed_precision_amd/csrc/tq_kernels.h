@@ -34,6 +34,9 @@ hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_tq2_swiglu(const GemmArgs& a, const void* qs_up, const void* scales_up,
                              hipStream_t stream);
 int glu_rows(int64_t N);
+// Input gradient dX [M][K] = dY [M][N] (s . T) of a TQ2 matrix (N % 8 == 0).
+hipError_t launch_tq2_bwd_x(const void* dY, const void* qs, const void* scales, void* dX,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 // TQ1 MFMA kernel: any M, in slices of 16 activation rows.
 hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream);

@@ -206,6 +206,20 @@ int tq_gemm_tq2_swiglu(const void* X, const void* qs_gate, const void* scales_ga
                        const void* qs_up, const void* scales_up_f16, void* Y, int64_t M,
                        int64_t N, int64_t K, void* stream);
 
+/* Input gradient of the ternary product for quantization-aware training
+ * (the backward pass through "The model", step 3, on the project page
+ * "Scaling Laws and Efficient Inference for Ternary Language Models"):
+ *   dX[m][k] = sum_n dY[m][n] * scales[n][k/256] * T[n][k],
+ * i.e. dY (s . T) with the TQ2 matrix of tq_gemm_tq2 (qs [N][K/4], scales
+ * [N][K/256] fp16) read the other way round; dY [M][N] and dX [M][K] fp16,
+ * device pointers, 16-byte aligned, owned by the caller; FP32 accumulation,
+ * one fp16 rounding.  N must be a positive multiple of 8, K a multiple of 256
+ * (TQ_ERR_SHAPE otherwise); M = 0 is a no-op returning TQ_OK.  The weight
+ * gradient under the straight-through estimator, dY^T X, is a plain dense
+ * product left to the caller's BLAS. */
+int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales_f16, void* dX,
+                      int64_t M, int64_t N, int64_t K, void* stream);
+
 /* As tq_gemm_tq2_tiled with the weight rows per wave explicit: 16 mt
  * activation rows x 16 nr ng weight rows per workgroup of ng x kg waves.
  * Compiled tiles (mt, nr, ng, kg): mt in {2, 4} with (4, 4, 2), (4, 2, 4),

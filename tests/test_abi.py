@@ -213,3 +213,18 @@ def test_build_step_does_not_load_the_library():
             "print('bit_mixed_precision_amd.binding' in sys.modules)") % ROOT
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, check=True)
     assert out.stdout.strip() == "False"
+
+
+def _bx(dY=A, q=A, s=A, dX=A, M=4, N=64, K=512):
+    return tq.raw_call("tq_gemm_tq2_bwd_x", dY, q, s, dX, M, N, K, None)
+
+
+def test_bwd_x_argument_errors():
+    assert _bx(M=0, dY=None) == tq.TQ_OK
+    assert _bx(M=-1) == tq.TQ_ERR_SHAPE
+    assert _bx(dX=None) == tq.TQ_ERR_NULL
+    assert _bx(q=None) == tq.TQ_ERR_NULL
+    assert _bx(N=0) == tq.TQ_ERR_SHAPE
+    assert _bx(N=60) == tq.TQ_ERR_SHAPE
+    assert _bx(K=300) == tq.TQ_ERR_SHAPE
+    assert _bx(dY=A + 8) == tq.TQ_ERR_ALIGN

@@ -419,6 +419,39 @@ def test_qkv_as_one_product():
             n0 += n
 
 
+# ---- QAT backward: input gradient through the ternary matrix
+
+BWD_SHAPES = [(1, 8, 256), (5, 40, 512), (130, 264, 768), (257, 1000, 1280), (64, 2048, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", BWD_SHAPES)
+def test_bwd_x_parity(M, N, K):
+    """dX = dY (s . T) against the fp64 oracle: ragged M (tiles of 128 rows),
+    N in chunks of 32 with a ragged tail, K over several 128-column tiles."""
+    from oracle import gemm_bwd_x_ref
+    say(f"[bwd_x] M={M} N={N} K={K}")
+    T, s = iid_problem(N, K, 0.31, 61)
+    dY = activations(M, N, 62)
+    dX = torch.full((M, K), float("nan"), dtype=torch.float16, device="cuda")
+    tq.tq_gemm_tq2_bwd_x(dev(dY), dev(pack("tq2", T)), dev(s), dX)
+    torch.cuda.synchronize()
+    check_close(dX.cpu().numpy(), gemm_bwd_x_ref(dY, T, s), f"bwd_x {M}x{N}x{K}")
+
+
+def test_bwd_x_adjoint_of_forward():
+    """<Y, dY> = <X, dX> for Y from tq_gemm_tq2 and dX from the backward, both
+    on the device (fp16 outputs, so within their rounding)."""
+    M, N, K = 16, 512, 1024
+    T, s = iid_problem(N, K, 0.31, 63)
+    q = dev(pack("tq2", T))
+    X, dY = activations(M, K, 64), activations(M, N, 65)
+    Y = tq.tq_gemm_tq2(dev(X), q, dev(s)).cpu().numpy().astype(np.float64)
+    dX = tq.tq_gemm_tq2_bwd_x(dev(dY), q, dev(s)).cpu().numpy().astype(np.float64)
+    lhs, rhs = float(np.sum(Y * dY)), float(np.sum(X.astype(np.float64) * dX))
+    scale = float(np.sum(np.abs(Y * dY)))
+    assert abs(lhs - rhs) <= 2e-3 * scale, (lhs, rhs, scale)
+
+
 def test_empty_is_noop():
     X = torch.empty((0, 256), dtype=torch.float16, device="cuda")
     q = torch.empty((16, 64), dtype=torch.uint8, device="cuda")
