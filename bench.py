@@ -40,8 +40,9 @@ def tq1_ldq(K):
 
 
 def alg_bytes(fmt, M, N, K):
-    """Bytes the method must move: packed weights, scales, X, Y."""
-    w = N * K // 4 if fmt == "tq2" else N * tq1_ldq(K)
+    """Bytes the method must move: packed weights, scales, X, Y (for "bwd":
+    dY [M][N] in, dX [M][K] out, the same sizes)."""
+    w = N * K // 4 if fmt in ("tq2", "bwd") else N * tq1_ldq(K)
     return w + 2 * N * (K // 256) + 2 * M * K + 2 * M * N
 
 
@@ -66,6 +67,11 @@ def workload_calls():
 
 PREFILL_MS = [256, 1024, 4096]
 
+# QAT backward: dX = dY (s . T) for the three weight shapes of a 70B layer
+# ((N, K) = (8192, 8192) for q / o, (28672, 8192) for gate / up, (8192,
+# 28672) for down) at 4096 tokens.
+BWD_CALLS = [("bwd", 4096, 8192, 8192), ("bwd", 4096, 28672, 8192), ("bwd", 4096, 8192, 28672)]
+
 
 def prefill_calls():
     """Prompt-sized products on the same two shapes (both formats)."""
@@ -88,7 +94,7 @@ def build_inputs(torch, tq, calls):
         rng = seed_for(500, N, K, 1 if fmt == "tq2" else 2)
         T = ternary_iid(rng, N, K, 0.31 if fmt == "tq2" else 0.3)
         s = block_scales_fp16(rng, N, K)
-        qs = tq.tq_pack_tq2(T)[0] if fmt == "tq2" else tq.tq_pack_tq1(T)[0]
+        qs = tq.tq_pack_tq1(T)[0] if fmt == "tq1" else tq.tq_pack_tq2(T)[0]
         del T
         per_set = qs.nbytes + s.nbytes
         R = max(2, -(-RING_BYTES // per_set))
@@ -97,11 +103,13 @@ def build_inputs(torch, tq, calls):
         ring = [(q0, s0)] + [(q0.clone(), s0.clone()) for _ in range(R - 1)]
         rings[key] = {"sets": ring, "next": 0}
         log(f"[bench] {fmt} N={N} K={K}: {R} buffer sets of {per_set / 1e6:.1f} MB")
-    xs = {}
+    xs, ys = {}, {}
     for fmt, M, N, K in calls:
-        if (M, K) not in xs:
-            xs[(M, K)] = torch.from_numpy(activations_fp16(seed_for(501, M, K), M, K)).cuda()
-    ys = {(M, N): torch.empty((M, N), dtype=torch.float16, device="cuda") for _, M, N, _ in calls}
+        xin, yout = ((M, N), (M, K)) if fmt == "bwd" else ((M, K), (M, N))
+        if xin not in xs:
+            xs[xin] = torch.from_numpy(activations_fp16(seed_for(501, *xin), *xin)).cuda()
+        if yout not in ys:
+            ys[yout] = torch.empty(yout, dtype=torch.float16, device="cuda")
     return rings, xs, ys
 
 
@@ -109,6 +117,13 @@ def run_call(tq, fmt, M, N, K, rings, xs, ys, stream):
     r = rings[(fmt, N, K)]
     q, s = r["sets"][r["next"]]
     r["next"] = (r["next"] + 1) % len(r["sets"])
+    if fmt == "bwd":
+        dY, dX = xs[(M, N)], ys[(M, K)]
+        st = tq.lib.tq_gemm_tq2_bwd_x(dY.data_ptr(), q.data_ptr(), s.data_ptr(), dX.data_ptr(),
+                                      M, N, K, stream)
+        if st != 0:
+            raise RuntimeError(f"tq_gemm_tq2_bwd_x failed: {tq.tq_status_string(st)}")
+        return
     X, Y = xs[(M, K)], ys[(M, N)]
     if fmt == "tq2":
         st = tq.lib.tq_gemm_tq2(X.data_ptr(), q.data_ptr(), s.data_ptr(), Y.data_ptr(), M, N, K,
@@ -192,7 +207,8 @@ def gpu_bench(args, calls):
         tr = t_roof(fmt, M, N, K)
         per_call.append({
             "fmt": fmt, "M": M, "N": N, "K": K,
-            "kernel": tq.tq_kernel_name(2 if fmt == "tq2" else 1, M, N, K),
+            "kernel": "tq2_bwd_x_kernel" if fmt == "bwd" else
+                      tq.tq_kernel_name(2 if fmt == "tq2" else 1, M, N, K),
             "us": round(us, 3), "TBps": round(b / us / 1e6, 3), "TFLOPps": round(f / us / 1e6, 2),
             "bound": "hbm" if b / HBM_PEAK >= f / MFMA_F16_PEAK else "mfma",
             "hbm_frac": round(b / HBM_PEAK / (us * 1e-6), 4),
@@ -259,7 +275,7 @@ def roofline_of(per_call):
 def cpu_baseline(calls, cols=1024):
     """The fp64 oracle on the host: each call of the step on ``cols`` sampled
     output columns, time scaled by N / cols."""
-    from oracle import gemm_ref
+    from oracle import gemm_bwd_x_ref, gemm_ref
     from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
     try:
         from threadpoolctl import threadpool_info
@@ -269,15 +285,24 @@ def cpu_baseline(calls, cols=1024):
     weights = {}
     total_t = total_roof = total_bytes = total_flops = 0.0
     for fmt, M, N, K in calls:
-        key = (fmt, K)
-        if key not in weights:
-            rng = seed_for(600, K, 1 if fmt == "tq2" else 2)
-            weights[key] = (ternary_iid(rng, cols, K, 0.31), block_scales_fp16(rng, cols, K))
-        T, s = weights[key]
-        X = activations_fp16(seed_for(601, M, K), M, K)
-        t = time.perf_counter()
-        gemm_ref(X, T, s)
-        dt = (time.perf_counter() - t) * (N / cols)
+        if fmt == "bwd":  # dX on `cols` sampled columns k: the full N x cols weight slice
+            rng = seed_for(602, N, K)
+            T = ternary_iid(rng, N, 256, 0.31)
+            s = block_scales_fp16(rng, N, 256)
+            dY = activations_fp16(seed_for(603, M, N), M, N)
+            t = time.perf_counter()
+            gemm_bwd_x_ref(dY, T, s)
+            dt = (time.perf_counter() - t) * (K / 256)
+        else:
+            key = (fmt, K)
+            if key not in weights:
+                rng = seed_for(600, K, 1 if fmt == "tq2" else 2)
+                weights[key] = (ternary_iid(rng, cols, K, 0.31), block_scales_fp16(rng, cols, K))
+            T, s = weights[key]
+            X = activations_fp16(seed_for(601, M, K), M, K)
+            t = time.perf_counter()
+            gemm_ref(X, T, s)
+            dt = (time.perf_counter() - t) * (N / cols)
         total_t += dt
         total_roof += t_roof(fmt, M, N, K)
         total_bytes += alg_bytes(fmt, M, N, K)
@@ -497,6 +522,8 @@ def main():
     ap.add_argument("--reps", type=int, default=30, help="launches per call when timing each call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calls-out", default=None, help="also write the per-call table here (JSON)")
+    ap.add_argument("--bwd", action="store_true",
+                    help="QAT backward dX = dY (s.T) at the 70B layer shapes, 4096 tokens")
     ap.add_argument("--stack", action="store_true",
                     help="the 560 linears of an 80-layer stack, back to back in one HIP graph")
     ap.add_argument("--pack", action="store_true",
@@ -554,12 +581,38 @@ def main():
             out["cpu_baseline"] = pack_cpu_baseline()
         print(json.dumps(out), flush=True)
         return
-    calls = prefill_calls() if args.prefill else workload_calls()
-    if args.prefill:
+    calls = BWD_CALLS if args.bwd else prefill_calls() if args.prefill else workload_calls()
+    if args.prefill or args.bwd:
         args.reps = min(args.reps, 3)
     calls, per_call, ms_step = gpu_bench(args, calls)
     roof_sum = sum(t_roof(*c) for c in calls)
     value = roof_sum / (ms_step * 1e-3)
+    if args.bwd:
+        out = {
+            "metric": "QAT backward dX = dY (s.T) TFLOP/s vs FP16 MFMA peak, 70B layer shapes at "
+                      "4096 tokens",
+            "value": round(value, 4),
+            "unit": "fraction of roofline (FP16 MFMA 2.5 PFLOP/s; every call is MFMA-bound)",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16", "data": "synthetic",
+            "config": {"workload": "dX for (N,K) in {(8192,8192),(28672,8192),(8192,28672)}, "
+                                   "M=4096 tokens; i.i.d. trits, fp16 block scales",
+                       "global_batch": None, "seq_len": None, "parallelism": "none"},
+            "roofline": roofline_of(per_call),
+            "tflops_total": round(sum(alg_flops(*c[1:]) for c in calls) / (ms_step * 1e-3) / 1e12,
+                                  1),
+        }
+        if not args.no_cpu_baseline:
+            log("[bench] CPU baseline (oracle) ...")
+            cb = cpu_baseline(calls)
+            cb["sample"] = "every call on 256 sampled columns k (the full N x 256 weight slice, fp64 " \
+                           "dequantize + numpy matmul), time scaled by K/256"
+            out["cpu_baseline"] = cb
+        out["calls"] = per_call
+        print(json.dumps(out), flush=True)
+        return
     if args.prefill:
         out = {
             "metric": "ternary GEMM TFLOP/s vs FP16 MFMA peak at prefill sizes M=256..4096, K=8192 "
