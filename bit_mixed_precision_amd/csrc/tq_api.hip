@@ -13,6 +13,7 @@ namespace {
 
 constexpr int64_t kMaxMN = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 20;
+constexpr int64_t kMaxBwdN = int64_t(1) << 20;  // 32-bit offsets in 512 rows of dY
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -222,7 +223,7 @@ int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales, void* 
   if (M < 0 || N < 0) return TQ_ERR_SHAPE;
   if (M == 0) return TQ_OK;
   if (!dY || !qs || !scales || !dX) return TQ_ERR_NULL;
-  if (N == 0 || N % 8 || M > kMaxMN || N > kMaxMN || K < 256 || K % 256 || K > kMaxK)
+  if (N == 0 || N % 8 || M > kMaxMN || N > kMaxBwdN || K < 256 || K % 256 || K > kMaxK)
     return TQ_ERR_SHAPE;
   if (!aligned16(dY) || !aligned16(qs) || !aligned16(scales) || !aligned16(dX)) return TQ_ERR_ALIGN;
   int st = device_ready();

@@ -213,8 +213,10 @@ int tq_gemm_tq2_swiglu(const void* X, const void* qs_gate, const void* scales_ga
  * i.e. dY (s . T) with the TQ2 matrix of tq_gemm_tq2 (qs [N][K/4], scales
  * [N][K/256] fp16) read the other way round; dY [M][N] and dX [M][K] fp16,
  * device pointers, 16-byte aligned, owned by the caller; FP32 accumulation,
- * one fp16 rounding.  N must be a positive multiple of 8, K a multiple of 256
- * (TQ_ERR_SHAPE otherwise); M = 0 is a no-op returning TQ_OK.  The weight
+ * one fp16 rounding.  N must be a positive multiple of 8 and at most 2^20, K
+ * a multiple of 256 (TQ_ERR_SHAPE otherwise); M = 0 is a no-op returning
+ * TQ_OK.  Block scales must satisfy |s| < 1024: the kernel carries a column's
+ * field position as an exact factor of up to 64 on the decoded s.  The weight
  * gradient under the straight-through estimator, dY^T X, is a plain dense
  * product left to the caller's BLAS. */
 int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales_f16, void* dX,

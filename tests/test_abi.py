@@ -226,5 +226,6 @@ def test_bwd_x_argument_errors():
     assert _bx(q=None) == tq.TQ_ERR_NULL
     assert _bx(N=0) == tq.TQ_ERR_SHAPE
     assert _bx(N=60) == tq.TQ_ERR_SHAPE
+    assert _bx(N=(1 << 20) + 8) == tq.TQ_ERR_SHAPE  # past the 32-bit offsets of 512 rows
     assert _bx(K=300) == tq.TQ_ERR_SHAPE
     assert _bx(dY=A + 8) == tq.TQ_ERR_ALIGN
