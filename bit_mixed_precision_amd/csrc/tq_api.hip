@@ -170,8 +170,9 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
   if (c.launch == tq::launch_tq1_skinny)
     snprintf(buf, sizeof buf, "%s<%d, %s, %d>", c.name, c.variant, c.variant2 ? "true" : "false",
              c.variant3);
-  else if (c.variant2 >= 0 && c.launch == tq::launch_tq2_skinny)
-    snprintf(buf, sizeof buf, "%s<%d, %s>", c.name, c.variant, c.variant2 ? "true" : "false");
+  else if (c.variant2 >= 0 && c.launch == tq::launch_tq2_skinny)  // plain product: GLU = false
+    snprintf(buf, sizeof buf, "%s<%d, %s, false>", c.name, c.variant,
+             c.variant2 ? "true" : "false");
   else if (c.variant5 >= 0)
     snprintf(buf, sizeof buf, "%s<%d, %d, %d, %d, %d>", c.name, c.variant, c.variant2,
              c.variant3, c.variant4, c.variant5);
