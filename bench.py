@@ -218,6 +218,79 @@ def gpu_bench(args, calls):
     return calls, per_call, ms_step
 
 
+def context_bench(calls, per_call):
+    """Context beside the metric (not part of `value`): the practical read
+    ceiling -- one plain streaming-read launch of the bytes an M = 1 TQ2 call
+    streams, timed like the calls (a graph of back-to-back launches over
+    rotating buffers of at least 1 GiB) -- and torch's FP16 matmul on the TQ2
+    sweep shapes, with FP16 weights rotating the same way, for the speedup of
+    the packed kernels over plain FP16 weights."""
+    import torch
+    import bit_mixed_precision_amd.binding as tq
+
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    shapes = sorted({(N, K) for fmt, M, N, K in calls if fmt == "tq2"})
+    out = {"read_ceiling": [], "fp16_matmul": []}
+    ceiling = {}
+    reps = 60
+    for N, K in shapes:
+        nbytes = alg_bytes("tq2", 1, N, K) // 16 * 16
+        R = max(2, -(-RING_BYTES // nbytes))
+        bufs = [torch.zeros(nbytes, dtype=torch.uint8, device="cuda") for _ in range(R)]
+        cap = torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(reps):
+                    st = tq.lib.tq_stream_read(bufs[i % R].data_ptr(), nbytes, sink.data_ptr(),
+                                               cap.cuda_stream)
+                    if st != 0:
+                        raise RuntimeError(f"tq_stream_read failed: {tq.tq_status_string(st)}")
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        ceiling[(N, K)] = us
+        out["read_ceiling"].append({"N": N, "K": K, "bytes": nbytes, "us": round(us, 3),
+                                    "TBps": round(nbytes / us / 1e6, 3),
+                                    "hbm_frac": round(nbytes / HBM_PEAK / (us * 1e-6), 4)})
+        del g, bufs
+    for c in per_call:
+        if c["fmt"] == "tq2" and c["M"] == 1 and (c["N"], c["K"]) in ceiling:
+            c["of_read_ceiling"] = round(ceiling[(c["N"], c["K"])] / c["us"], 4)
+    tq2_us = {(c["M"], c["N"], c["K"]): c["us"] for c in per_call if c["fmt"] == "tq2"}
+    for N, K in shapes:
+        R = max(2, -(-RING_BYTES // (K * N * 2)))
+        gen = torch.Generator(device="cuda").manual_seed(502)
+        w = [torch.randn(K, N, device="cuda", dtype=torch.float16, generator=gen) * 0.02
+             for _ in range(R)]
+        for M in sorted({M for fmt, M, n, k in calls if fmt == "tq2" and (n, k) == (N, K)}):
+            X = torch.randn(M, K, device="cuda", dtype=torch.float16, generator=gen)
+            Y = torch.empty(M, N, device="cuda", dtype=torch.float16)
+            for i in range(R):
+                torch.mm(X, w[i], out=Y)
+            torch.cuda.synchronize()
+            n_mm = 30
+            e0.record(stream)
+            for i in range(n_mm):
+                torch.mm(X, w[i % R], out=Y)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / n_mm * 1e3
+            t2 = tq2_us[(M, N, K)]
+            out["fp16_matmul"].append({"M": M, "N": N, "K": K, "us": round(us, 3),
+                                       "TFLOPps": round(alg_flops(M, N, K) / us / 1e6, 2),
+                                       "tq2_us": t2, "tq2_speedup": round(us / t2, 2)})
+        del w
+    return out
+
+
 def kernel_source_sha():
     """sha256 (first 16 hex) over the kernel sources, as recorded with the counters."""
     import glob
@@ -521,6 +594,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--reps", type=int, default=30, help="launches per call when timing each call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the read-ceiling and FP16-matmul context of the sweep")
     ap.add_argument("--calls-out", default=None, help="also write the per-call table here (JSON)")
     ap.add_argument("--bwd", action="store_true",
                     help="QAT backward dX = dY (s.T) at the 70B layer shapes, 4096 tokens")
@@ -653,6 +728,9 @@ def main():
     mf = [c for c in per_call if c["bound"] == "mfma"]
     out["hbm_bound_calls"] = {"n": len(hbm), "mean_hbm_frac": round(float(np.mean([c["hbm_frac"] for c in hbm])), 4) if hbm else None}
     out["mfma_bound_calls"] = {"n": len(mf), "mean_mfma_frac": round(float(np.mean([c["mfma_frac"] for c in mf])), 4) if mf else None}
+    if not args.no_context:
+        log("[bench] context: read ceiling and FP16 matmul ...")
+        out["context"] = context_bench(calls, per_call)
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(calls)

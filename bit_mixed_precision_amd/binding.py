@@ -59,6 +59,7 @@ SIGNATURES = {
     "tq_gemm_tq2_tile": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P]),
     "tq_gemm_tq2_swiglu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_gemm_tq2_bwd_x": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "tq_stream_read": (_I, [_P, _I64, _P, _P]),
     "tq_gemm_tq1_tiled": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_pack_dev_workspace_bytes": (_I64, [_I64, _I64]),
     "tq_pack_tq2_dev": (_I, [_P, _I64, _I64, C.c_double, _P, _P, _P, _P, _P, _I64, _P]),
@@ -243,6 +244,13 @@ def tq_gemm_tq2_bwd_x(dY, qs, scales, dX=None, stream=None):
     _check(lib.tq_gemm_tq2_bwd_x(_ptr(dY), _ptr(qs), _ptr(scales), _ptr(dX), M, N, K,
                                  _stream(stream)), "tq_gemm_tq2_bwd_x")
     return dX
+
+
+def tq_stream_read(src, sink, stream=None):
+    """Read every byte of the contiguous device tensor src once (the practical
+    read ceiling); sink is a device tensor of at least 4 bytes."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib.tq_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "tq_stream_read")
 
 
 def tq_gemm_tq2_tile(X, qs, scales, mt: int, nr: int, ng: int, kg: int, Y=None, stream=None):

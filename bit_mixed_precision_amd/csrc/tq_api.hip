@@ -232,6 +232,16 @@ int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales, void* 
   return finish(tq::launch_tq2_bwd_x(dY, qs, scales, dX, M, N, K, static_cast<hipStream_t>(stream)));
 }
 
+int tq_stream_read(const void* src, int64_t bytes, void* sink, void* stream) {
+  if (bytes < 0 || bytes % 16) return TQ_ERR_SHAPE;
+  if (bytes == 0) return TQ_OK;
+  if (!src || !sink) return TQ_ERR_NULL;
+  if (!aligned16(src) || !aligned16(sink)) return TQ_ERR_ALIGN;
+  int st = device_ready();
+  if (st != TQ_OK) return st;
+  return finish(tq::launch_stream_read(src, bytes, sink, static_cast<hipStream_t>(stream)));
+}
+
 int tq_gemm_tq2_tile(const void* X, const void* qs, const void* scales, void* Y, int64_t M,
                      int64_t N, int64_t K, int mt, int nr, int ng, int kg, void* stream) {
   bool noop = false;

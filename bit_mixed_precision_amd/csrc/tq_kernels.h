@@ -67,4 +67,8 @@ int tq1_tiled_xahead(const Tq1TiledShape& t);    // stages the activations are l
 hipError_t launch_tq1_tiled(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_tq1_tiled_shape(const Tq1TiledShape& t, const GemmArgs& a, hipStream_t stream);
 
+// Plain streaming read of `bytes` (a multiple of 16) at src; sink gets a
+// write only if the folded data equals one fixed value.
+hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t stream);
+
 }  // namespace tq

@@ -222,6 +222,18 @@ int tq_gemm_tq2_swiglu(const void* X, const void* qs_gate, const void* scales_ga
 int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales_f16, void* dX,
                       int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Measurement aid: the practical read ceiling for the weight-streaming
+ * kernels.  Small-batch ternary inference is bound by reading the packed
+ * weights ("TriRun: ternary inference on GPUs" on the project page "Scaling
+ * Laws and Efficient Inference for Ternary Language Models"); this reads
+ * `bytes` bytes at `src` once, with the loads the GEMV kernels use, and
+ * computes nothing, so its time at a given size is what a launch that only
+ * streams those bytes costs on this GPU.  src and sink are device pointers,
+ * 16-byte aligned, owned by the caller; sink (4 bytes) is written only when
+ * the XOR of the data equals one fixed 32-bit value.  bytes must be a
+ * non-negative multiple of 16 (TQ_ERR_SHAPE otherwise); 0 is a no-op. */
+int tq_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
+
 /* As tq_gemm_tq2_tiled with the weight rows per wave explicit: 16 mt
  * activation rows x 16 nr ng weight rows per workgroup of ng x kg waves.
  * Compiled tiles (mt, nr, ng, kg): mt in {2, 4} with (4, 4, 2), (4, 2, 4),

@@ -229,3 +229,12 @@ def test_bwd_x_argument_errors():
     assert _bx(N=(1 << 20) + 8) == tq.TQ_ERR_SHAPE  # past the 32-bit offsets of 512 rows
     assert _bx(K=300) == tq.TQ_ERR_SHAPE
     assert _bx(dY=A + 8) == tq.TQ_ERR_ALIGN
+
+
+def test_stream_read_argument_errors():
+    assert tq.raw_call("tq_stream_read", A, 0, A, None) == tq.TQ_OK
+    assert tq.raw_call("tq_stream_read", A, -16, A, None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_stream_read", A, 40, A, None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_stream_read", None, 64, A, None) == tq.TQ_ERR_NULL
+    assert tq.raw_call("tq_stream_read", A, 64, None, None) == tq.TQ_ERR_NULL
+    assert tq.raw_call("tq_stream_read", A + 4, 64, A, None) == tq.TQ_ERR_ALIGN

@@ -452,6 +452,25 @@ def test_bwd_x_adjoint_of_forward():
     assert abs(lhs - rhs) <= 2e-3 * scale, (lhs, rhs, scale)
 
 
+def test_stream_read_covers_every_piece():
+    """The read-ceiling kernel folds every 16-byte piece: a lone piece whose
+    dwords XOR to the marker is found wherever it sits; zeros write nothing."""
+    marker = 0x9E3779B9 - (1 << 32)  # as int32
+    n = (1 << 20) + 48  # not a multiple of the 256 x 512 x 4 pieces of one sweep
+    src = torch.zeros(n // 4, dtype=torch.int32, device="cuda")
+    sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
+    tq.tq_stream_read(src, sink)
+    torch.cuda.synchronize()
+    assert int(sink[0]) == 7
+    for piece in (0, 1, 4095, n // 32, n // 16 - 1):
+        src.zero_()
+        src[4 * piece] = marker
+        sink.fill_(7)
+        tq.tq_stream_read(src, sink)
+        torch.cuda.synchronize()
+        assert int(sink[0]) == marker, piece
+
+
 def test_empty_is_noop():
     X = torch.empty((0, 256), dtype=torch.float16, device="cuda")
     q = torch.empty((16, 64), dtype=torch.uint8, device="cuda")
