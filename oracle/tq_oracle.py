@@ -282,12 +282,20 @@ def swiglu_ref(X, T_gate, s_gate, T_up, s_up, cols=None) -> np.ndarray:
     return silu_ref(g) * u
 
 
-def gemm_bwd_x_ref(dY, T, scales) -> np.ndarray:
+def gemm_bwd_x_ref(dY, T, scales, cols=None) -> np.ndarray:
     """dX = dY (s . T) in fp64: the input gradient of Y = X (s . T)^T (the
     backward pass of quantization-aware training, "The model": the forward
-    uses the ternary weights, the backward the same product transposed)."""
+    uses the ternary weights, the backward the same product transposed).
+    ``cols`` restricts the output columns k (the same product, fewer columns
+    of s . T)."""
     dY64 = np.asarray(dY).astype(np.float64)
-    Wd = dequantize_ref(T, scales)
+    if cols is None:
+        Wd = dequantize_ref(T, scales)
+    else:
+        cols = np.asarray(cols)
+        T = np.asarray(T)
+        s64 = np.asarray(scales).astype(np.float64)
+        Wd = s64[:, cols // 256] * T[:, cols].astype(np.float64)
     if dY64.shape[1] != Wd.shape[0]:
         raise ValueError("dY and T disagree on N")
     return dY64 @ Wd

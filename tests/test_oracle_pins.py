@@ -389,3 +389,17 @@ def test_bwd_x_adjoint():
         for k in (0, 255, 256, 511):
             want = math.fsum(float(dY[m, n]) * float(s[n, k // 256]) * int(T[n, k]) for n in range(N))
             assert abs(G[m, k] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def test_bwd_x_column_sampling():
+    """The sampled form of the backward oracle is the full product's columns
+    (block boundaries at 255/256 and the last column included)."""
+    from oracle import gemm_bwd_x_ref
+    rng = np.random.default_rng(81)
+    N, K, M = 24, 768, 5
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    s = rng.uniform(0.01, 0.03, size=(N, K // 256)).astype(np.float16)
+    dY = rng.standard_normal((M, N)).astype(np.float16)
+    cols = np.array([0, 255, 256, 511, 700, K - 1])
+    full = gemm_bwd_x_ref(dY, T, s)
+    np.testing.assert_array_equal(gemm_bwd_x_ref(dY, T, s, cols=cols), full[:, cols])
