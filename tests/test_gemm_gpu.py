@@ -438,6 +438,60 @@ def test_bwd_x_parity(M, N, K):
     check_close(dX.cpu().numpy(), gemm_bwd_x_ref(dY, T, s), f"bwd_x {M}x{N}x{K}")
 
 
+def test_bwd_x_exact_integers():
+    """Integer dY in [-3, 3] and scales in {1/4, 1/2, 1, 2}: every partial sum
+    is exact in fp32, so dX must equal the oracle rounded once to fp16, value
+    for value.  Two 512-row tiles (the second ragged) and a ragged last chunk
+    of n."""
+    from oracle import gemm_bwd_x_ref
+    M, N, K = 520, 264, 768
+    rng = np.random.default_rng(71)
+    T = rng.integers(-1, 2, size=(N, K)).astype(np.int8)
+    s = (2.0 ** rng.integers(-2, 2, size=(N, K // 256))).astype(np.float16)
+    dY = rng.integers(-3, 4, size=(M, N)).astype(np.float16)
+    say(f"[bwd_x exact] M={M} N={N} K={K}")
+    dX = tq.tq_gemm_tq2_bwd_x(dev(dY), dev(pack("tq2", T)), dev(s)).cpu().numpy()
+    ref = gemm_bwd_x_ref(dY, T, s).astype(np.float16)
+    assert np.array_equal(dX.astype(np.float64), ref.astype(np.float64))
+
+
+@pytest.mark.parametrize("kind", ["large", "subnormal"])
+def test_bwd_x_scale_extremes(kind):
+    """Scales near the documented bound (|s| = 1000: the kernel carries up to
+    64 s in fp16) and fp16-subnormal scales (2^-20, 3 * 2^-24): finite and
+    within the bound."""
+    from oracle import gemm_bwd_x_ref
+    M, N, K = 64, 96, 1024
+    T, _ = iid_problem(N, K, 0.31, 72)
+    rng = np.random.default_rng(73)
+    if kind == "large":
+        s = rng.choice(np.array([1000.0, -1000.0, 999.5, 512.0]), size=(N, K // 256))
+        dY = rng.standard_normal((M, N)) * 0.01
+    else:
+        s = rng.choice(np.array([2.0 ** -20, 3 * 2.0 ** -24, -(2.0 ** -17)]), size=(N, K // 256))
+        dY = rng.standard_normal((M, N)) * 100.0
+    s, dY = s.astype(np.float16), dY.astype(np.float16)
+    say(f"[bwd_x scales {kind}]")
+    dX = tq.tq_gemm_tq2_bwd_x(dev(dY), dev(pack("tq2", T)), dev(s))
+    torch.cuda.synchronize()
+    check_close(dX.cpu().numpy(), gemm_bwd_x_ref(dY, T, s), f"bwd_x scales {kind}")
+
+
+def test_bwd_x_full_size_sampled():
+    """The bench's launch at full size, M = 4096 tokens, N = K = 8192: sampled
+    columns k (both sides of scale-block and 128-column tile boundaries, the
+    last column) against the oracle."""
+    from oracle import gemm_bwd_x_ref
+    M, N, K = 4096, 8192, 8192
+    T, s = iid_problem(N, K, 0.31, 74)
+    dY = activations(M, N, 75)
+    say(f"[bwd_x full] M={M} N={N} K={K}")
+    dX = tq.tq_gemm_tq2_bwd_x(dev(dY), dev(pack("tq2", T)), dev(s))
+    torch.cuda.synchronize()
+    cols = np.array([0, 1, 127, 128, 255, 256, 4095, 4096, 8190, 8191])
+    check_close(dX[:, cols].cpu().numpy(), gemm_bwd_x_ref(dY, T, s, cols=cols), "bwd_x full")
+
+
 def test_bwd_x_adjoint_of_forward():
     """<Y, dY> = <X, dX> for Y from tq_gemm_tq2 and dX from the backward, both
     on the device (fp16 outputs, so within their rounding)."""
