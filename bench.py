@@ -110,6 +110,8 @@ def build_inputs(torch, tq, calls):
             xs[xin] = torch.from_numpy(activations_fp16(seed_for(501, *xin), *xin)).cuda()
         if yout not in ys:
             ys[yout] = torch.empty(yout, dtype=torch.float16, device="cuda")
+        if fmt == "tq1" and M >= tq.tq_tq1_transcode_min_m() and ("ws", N, K) not in xs:
+            xs[("ws", N, K)] = torch.empty(N * K // 4, dtype=torch.uint8, device="cuda")
     return rings, xs, ys
 
 
@@ -128,11 +130,26 @@ def run_call(tq, fmt, M, N, K, rings, xs, ys, stream):
     if fmt == "tq2":
         st = tq.lib.tq_gemm_tq2(X.data_ptr(), q.data_ptr(), s.data_ptr(), Y.data_ptr(), M, N, K,
                                 stream)
+    elif M >= tq.tq_tq1_transcode_min_m():
+        # batch and prefill sizes: transcode once per call into the workspace,
+        # then the TQ2 kernels (both inside the timed call)
+        ws = xs[("ws", N, K)]
+        st = tq.lib.tq_gemm_tq1_ws(X.data_ptr(), q.data_ptr(), q.shape[1], s.data_ptr(),
+                                   Y.data_ptr(), M, N, K, ws.data_ptr(), ws.numel(), stream)
     else:
         st = tq.lib.tq_gemm_tq1(X.data_ptr(), q.data_ptr(), q.shape[1], s.data_ptr(),
                                 Y.data_ptr(), M, N, K, stream)
     if st != 0:
         raise RuntimeError(f"tq_gemm_{fmt} failed: {tq.tq_status_string(st)}")
+
+
+def kernel_label(tq, fmt, M, N, K):
+    """The kernel(s) a call runs, as profilers name them."""
+    if fmt == "bwd":
+        return "tq2_bwd_x_kernel"
+    if fmt == "tq1" and M >= tq.tq_tq1_transcode_min_m():
+        return "tq1_to_tq2_kernel + " + tq.tq_kernel_name(2, M, N, K)
+    return tq.tq_kernel_name(2 if fmt == "tq2" else 1, M, N, K)
 
 
 def gpu_bench(args, calls):
@@ -207,8 +224,7 @@ def gpu_bench(args, calls):
         tr = t_roof(fmt, M, N, K)
         per_call.append({
             "fmt": fmt, "M": M, "N": N, "K": K,
-            "kernel": "tq2_bwd_x_kernel" if fmt == "bwd" else
-                      tq.tq_kernel_name(2 if fmt == "tq2" else 1, M, N, K),
+            "kernel": kernel_label(tq, fmt, M, N, K),
             "us": round(us, 3), "TBps": round(b / us / 1e6, 3), "TFLOPps": round(f / us / 1e6, 2),
             "bound": "hbm" if b / HBM_PEAK >= f / MFMA_F16_PEAK else "mfma",
             "hbm_frac": round(b / HBM_PEAK / (us * 1e-6), 4),

@@ -60,6 +60,9 @@ SIGNATURES = {
     "tq_gemm_tq2_swiglu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_gemm_tq2_bwd_x": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_stream_read": (_I, [_P, _I64, _P, _P]),
+    "tq_transcode_tq1_tq2": (_I, [_P, _I64, _I64, _I64, _P, _P]),
+    "tq_tq1_transcode_min_m": (_I, []),
+    "tq_gemm_tq1_ws": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "tq_gemm_tq1_tiled": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_pack_dev_workspace_bytes": (_I64, [_I64, _I64]),
     "tq_pack_tq2_dev": (_I, [_P, _I64, _I64, C.c_double, _P, _P, _P, _P, _P, _I64, _P]),
@@ -244,6 +247,35 @@ def tq_gemm_tq2_bwd_x(dY, qs, scales, dX=None, stream=None):
     _check(lib.tq_gemm_tq2_bwd_x(_ptr(dY), _ptr(qs), _ptr(scales), _ptr(dX), M, N, K,
                                  _stream(stream)), "tq_gemm_tq2_bwd_x")
     return dX
+
+
+def tq_tq1_transcode_min_m() -> int:
+    """Activation rows from which tq_gemm_tq1_ws transcodes to TQ2."""
+    return int(lib.tq_tq1_transcode_min_m())
+
+
+def tq_transcode_tq1_tq2(qs1, K: int, qs2=None, stream=None):
+    """TQ2 bytes [N][K/4] (uint8, device) holding the trits of the TQ1 rows qs1 [N][ldq]."""
+    import torch
+    N, ldq = qs1.shape
+    if qs2 is None:
+        qs2 = torch.empty((N, K // 4), dtype=torch.uint8, device=qs1.device)
+    _check(lib.tq_transcode_tq1_tq2(_ptr(qs1), ldq, N, K, _ptr(qs2), _stream(stream)),
+           "tq_transcode_tq1_tq2")
+    return qs2
+
+
+def tq_gemm_tq1_ws(X, qs, scales, workspace, Y=None, stream=None):
+    """tq_gemm_tq1 with a workspace (uint8 device tensor of at least N * K / 4
+    bytes): from tq_tq1_transcode_min_m() rows on, the weights are transcoded
+    once into it and the TQ2 kernels run."""
+    M, K = X.shape
+    N, ldq = qs.shape
+    Y = _out(Y, M, N, X)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.tq_gemm_tq1_ws(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K,
+                              _ptr(workspace), nbytes, _stream(stream)), "tq_gemm_tq1_ws")
+    return Y
 
 
 def tq_stream_read(src, sink, stream=None):

@@ -14,6 +14,9 @@ namespace {
 constexpr int64_t kMaxMN = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxBwdN = int64_t(1) << 20;  // 32-bit offsets in 512 rows of dY
+// From this many activation rows on, TQ1 products with a workspace transcode
+// the weights once and run the TQ2 kernels (measured crossover at K = 8192).
+constexpr int64_t kTq1TranscodeMinM = 48;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -276,6 +279,39 @@ int tq_gemm_tq2(const void* X, const void* qs, const void* scales, void* Y, int6
 int tq_gemm_tq1(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,
                 int64_t M, int64_t N, int64_t K, void* stream) {
   return tq_gemm_tq1_ex(X, qs, ldq, scales, Y, M, N, K, TQ_PATH_AUTO, stream);
+}
+
+int tq_transcode_tq1_tq2(const void* qs1, int64_t ldq, int64_t N, int64_t K, void* qs2,
+                         void* stream) {
+  if (N < 0) return TQ_ERR_SHAPE;
+  if (N == 0) return TQ_OK;
+  if (!qs1 || !qs2) return TQ_ERR_NULL;
+  if (N > kMaxMN || K < 256 || K % 256 || K > kMaxK || ldq < (K + 4) / 5 || ldq % 16)
+    return TQ_ERR_SHAPE;
+  if (!aligned16(qs1) || !aligned16(qs2)) return TQ_ERR_ALIGN;
+  int st = device_ready();
+  if (st != TQ_OK) return st;
+  return finish(tq::launch_tq1_to_tq2(qs1, ldq, N, K, qs2, static_cast<hipStream_t>(stream)));
+}
+
+int tq_tq1_transcode_min_m(void) { return (int)kTq1TranscodeMinM; }
+
+int tq_gemm_tq1_ws(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,
+                   int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                   void* stream) {
+  bool noop = false;
+  int st = check_gemm(X, qs, scales, Y, M, N, K, true, ldq, &noop);
+  if (st != TQ_OK || noop) return st;
+  if (workspace_bytes < 0) return TQ_ERR_SHAPE;
+  if (workspace && !aligned16(workspace)) return TQ_ERR_ALIGN;
+  const bool transcode = M >= kTq1TranscodeMinM && workspace && workspace_bytes >= N * (K / 4);
+  if (!transcode) return tq_gemm_tq1_ex(X, qs, ldq, scales, Y, M, N, K, TQ_PATH_AUTO, stream);
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = finish(tq::launch_tq1_to_tq2(qs, ldq, N, K, workspace, s));
+  if (st != TQ_OK) return st;
+  return run(false, tq::GemmArgs{X, workspace, scales, Y, M, N, K, 0}, TQ_PATH_AUTO, s);
 }
 
 }  // extern "C"

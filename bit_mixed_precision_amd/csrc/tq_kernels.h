@@ -71,4 +71,8 @@ hipError_t launch_tq1_tiled_shape(const Tq1TiledShape& t, const GemmArgs& a, hip
 // write only if the folded data equals one fixed value.
 hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t stream);
 
+// TQ1 rows (ldq bytes each) -> TQ2 rows (K / 4 bytes each), the same trits.
+hipError_t launch_tq1_to_tq2(const void* qs1, int64_t ldq, int64_t N, int64_t K, void* qs2,
+                             hipStream_t stream);
+
 }  // namespace tq

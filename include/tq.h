@@ -222,6 +222,35 @@ int tq_gemm_tq2_swiglu(const void* X, const void* qs_gate, const void* scales_ga
 int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales_f16, void* dX,
                       int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Re-pack TQ1 weights as TQ2 on the device: the trits of qs1 ([N][ldq],
+ * "1.6 bits per weight" on the project page "Scaling Laws and Efficient
+ * Inference for Ternary Language Models") written as the 2-bit fields of qs2
+ * ([N][K/4], "2 bits per weight"), bit for bit what tq_pack_tq2 writes for
+ * the same trits; the block scales are shared unchanged.  Device pointers,
+ * 16-byte aligned, owned by the caller; qs2 holds tq_tq2_bytes(N, K) bytes.
+ * K a multiple of 256, ldq >= ceil(K/5) and a multiple of 16 (TQ_ERR_SHAPE
+ * otherwise); N = 0 is a no-op.  Byte values that no trit group encodes are
+ * not detected. */
+int tq_transcode_tq1_tq2(const void* qs1, int64_t ldq, int64_t N, int64_t K, void* qs2,
+                         void* stream);
+
+/* Activation rows from which tq_gemm_tq1_ws transcodes (48). */
+int tq_tq1_transcode_min_m(void);
+
+/* TQ1 product with a caller workspace, for batch and prefill sizes: with
+ * M >= tq_tq1_transcode_min_m() and workspace_bytes >= tq_tq2_bytes(N, K),
+ * the weights are first re-packed into the workspace as by
+ * tq_transcode_tq1_tq2 and the TQ2 kernels of tq_gemm_tq2 run on it (the
+ * TQ1 kernels decode every weight once per activation tile; this decodes it
+ * once per call), so Y equals tq_gemm_tq2's on the same trits bit for bit.
+ * Otherwise (smaller M, no or too small a workspace) it is tq_gemm_tq1.
+ * The workspace is device memory owned by the caller, 16-byte aligned when
+ * given (TQ_ERR_ALIGN otherwise), overwritten by the call; calls that
+ * overlap on one workspace race.  Everything else is as tq_gemm_tq1. */
+int tq_gemm_tq1_ws(const void* X, const void* qs, int64_t ldq, const void* scales_f16, void* Y,
+                   int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
+                   void* stream);
+
 /* Measurement aid: the practical read ceiling for the weight-streaming
  * kernels.  Small-batch ternary inference is bound by reading the packed
  * weights ("TriRun: ternary inference on GPUs" on the project page "Scaling

@@ -238,3 +238,25 @@ def test_stream_read_argument_errors():
     assert tq.raw_call("tq_stream_read", None, 64, A, None) == tq.TQ_ERR_NULL
     assert tq.raw_call("tq_stream_read", A, 64, None, None) == tq.TQ_ERR_NULL
     assert tq.raw_call("tq_stream_read", A + 4, 64, A, None) == tq.TQ_ERR_ALIGN
+
+
+def test_transcode_argument_errors():
+    assert tq.raw_call("tq_transcode_tq1_tq2", A, 1648, 0, 8192, A, None) == tq.TQ_OK
+    assert tq.raw_call("tq_transcode_tq1_tq2", A, 1648, -1, 8192, A, None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_transcode_tq1_tq2", None, 1648, 4, 8192, A, None) == tq.TQ_ERR_NULL
+    assert tq.raw_call("tq_transcode_tq1_tq2", A, 1648, 4, 8192, None, None) == tq.TQ_ERR_NULL
+    assert tq.raw_call("tq_transcode_tq1_tq2", A, 1632, 4, 8192, A, None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_transcode_tq1_tq2", A, 1650, 4, 8192, A, None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_transcode_tq1_tq2", A, 1648, 4, 8000, A, None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_transcode_tq1_tq2", A + 4, 1648, 4, 8192, A, None) == tq.TQ_ERR_ALIGN
+    assert tq.raw_call("tq_transcode_tq1_tq2", A, 1648, 4, 8192, A + 8, None) == tq.TQ_ERR_ALIGN
+
+
+def test_gemm_tq1_ws_argument_errors():
+    assert tq.tq_tq1_transcode_min_m() == 48
+    call = lambda ws=A, nb=1 << 20, M=64, X=A: tq.raw_call(
+        "tq_gemm_tq1_ws", X, A, 64, A, A, M, 16, 256, ws, nb, None)
+    assert call(M=0, X=None) == tq.TQ_OK
+    assert call(X=None) == tq.TQ_ERR_NULL
+    assert call(nb=-1) == tq.TQ_ERR_SHAPE
+    assert call(ws=A + 4) == tq.TQ_ERR_ALIGN

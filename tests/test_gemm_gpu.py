@@ -506,6 +506,66 @@ def test_bwd_x_adjoint_of_forward():
     assert abs(lhs - rhs) <= 2e-3 * scale, (lhs, rhs, scale)
 
 
+# ---- TQ1 -> TQ2 transcoding and the TQ1 product with a workspace
+
+@pytest.mark.parametrize("N,K,ldq", [(1, 256, None), (37, 768, None), (100, 1280, 272),
+                                     (513, 8192, None)])
+def test_transcode_matches_host_packer(N, K, ldq):
+    """Device re-packing of TQ1 bytes equals the host TQ2 packing of the same
+    trits, byte for byte (ragged units at the row end, a padded ldq)."""
+    T, _ = iid_problem(N, K, 0.31, 91)
+    q1 = pack("tq1", T) if ldq is None else pack_tq1_ref(T, ldq)
+    say(f"[transcode] N={N} K={K} ldq={q1.shape[1]}")
+    q2 = tq.tq_transcode_tq1_tq2(dev(q1), K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q2.cpu().numpy(), pack("tq2", T))
+
+
+@pytest.mark.parametrize("M", [47, 48, 64, 130])
+def test_gemm_tq1_ws(M):
+    """From 48 rows on the workspace product equals tq_gemm_tq2 on the same
+    trits bit for bit; below, it equals tq_gemm_tq1; both match the oracle."""
+    N, K = 200, 1024
+    T, s = iid_problem(N, K, 0.31, 92)
+    X = activations(M, K, 93)
+    ws = torch.empty(N * K // 4 + 64, dtype=torch.uint8, device="cuda")
+    say(f"[tq1 ws] M={M}")
+    Y = tq.tq_gemm_tq1_ws(dev(X), dev(pack("tq1", T)), dev(s), ws).cpu().numpy()
+    if M >= tq.tq_tq1_transcode_min_m():
+        Y2 = tq.tq_gemm_tq2(dev(X), dev(pack("tq2", T)), dev(s)).cpu().numpy()
+    else:
+        Y2 = tq.tq_gemm_tq1(dev(X), dev(pack("tq1", T)), dev(s)).cpu().numpy()
+    np.testing.assert_array_equal(Y.view(np.uint16), Y2.view(np.uint16))
+    check_close(Y, ref(X, T, s), f"tq1 ws M={M}")
+
+
+def test_gemm_tq1_ws_small_workspace_runs_tq1():
+    """A workspace smaller than N * K / 4 bytes is not used: the TQ1 kernels run."""
+    M, N, K = 64, 96, 512
+    T, s = iid_problem(N, K, 0.31, 94)
+    X = activations(M, K, 95)
+    ws = torch.full((N * K // 4 - 16,), 0xAB, dtype=torch.uint8, device="cuda")
+    Y = tq.tq_gemm_tq1_ws(dev(X), dev(pack("tq1", T)), dev(s), ws).cpu().numpy()
+    Y1 = tq.tq_gemm_tq1(dev(X), dev(pack("tq1", T)), dev(s)).cpu().numpy()
+    np.testing.assert_array_equal(Y.view(np.uint16), Y1.view(np.uint16))
+    assert bool((ws == 0xAB).all())
+
+
+@pytest.mark.parametrize("M,N", [(64, 28672), (256, 8192)])
+def test_gemm_tq1_ws_full_size(M, N):
+    """The sweep's TQ1 batch point and a prefill size through the workspace
+    path, sampled columns against the oracle."""
+    K = 8192
+    T, s = iid_problem(N, K, 0.3, 96)
+    X = activations(M, K, 97)
+    ws = torch.empty(N * K // 4, dtype=torch.uint8, device="cuda")
+    say(f"[tq1 ws full] M={M} N={N}")
+    Y = tq.tq_gemm_tq1_ws(dev(X), dev(pack("tq1", T)), dev(s), ws)
+    torch.cuda.synchronize()
+    cols = np.array([0, 1, 15, 16, N // 2, N - 1])
+    check_close(Y[:, cols].cpu().numpy(), ref(X, T, s, cols=cols), f"tq1 ws full M={M} N={N}")
+
+
 def test_stream_read_covers_every_piece():
     """The read-ceiling kernel folds every 16-byte piece: a lone piece whose
     dwords XOR to the marker is found wherever it sits; zeros write nothing."""
