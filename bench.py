@@ -110,7 +110,7 @@ def build_inputs(torch, tq, calls):
             xs[xin] = torch.from_numpy(activations_fp16(seed_for(501, *xin), *xin)).cuda()
         if yout not in ys:
             ys[yout] = torch.empty(yout, dtype=torch.float16, device="cuda")
-        if fmt == "tq1" and M >= tq.tq_tq1_transcode_min_m() and ("ws", N, K) not in xs:
+        if fmt == "tq1" and M >= tq.tq_tq1_transcode_min_m(N, K) and ("ws", N, K) not in xs:
             xs[("ws", N, K)] = torch.empty(N * K // 4, dtype=torch.uint8, device="cuda")
     return rings, xs, ys
 
@@ -130,7 +130,7 @@ def run_call(tq, fmt, M, N, K, rings, xs, ys, stream):
     if fmt == "tq2":
         st = tq.lib.tq_gemm_tq2(X.data_ptr(), q.data_ptr(), s.data_ptr(), Y.data_ptr(), M, N, K,
                                 stream)
-    elif M >= tq.tq_tq1_transcode_min_m():
+    elif M >= tq.tq_tq1_transcode_min_m(N, K):
         # batch and prefill sizes: transcode once per call into the workspace,
         # then the TQ2 kernels (both inside the timed call)
         ws = xs[("ws", N, K)]
@@ -147,7 +147,7 @@ def kernel_label(tq, fmt, M, N, K):
     """The kernel(s) a call runs, as profilers name them."""
     if fmt == "bwd":
         return "tq2_bwd_x_kernel"
-    if fmt == "tq1" and M >= tq.tq_tq1_transcode_min_m():
+    if fmt == "tq1" and M >= tq.tq_tq1_transcode_min_m(N, K):
         return "tq1_to_tq2_kernel + " + tq.tq_kernel_name(2, M, N, K)
     return tq.tq_kernel_name(2 if fmt == "tq2" else 1, M, N, K)
 

@@ -61,7 +61,7 @@ SIGNATURES = {
     "tq_gemm_tq2_bwd_x": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_stream_read": (_I, [_P, _I64, _P, _P]),
     "tq_transcode_tq1_tq2": (_I, [_P, _I64, _I64, _I64, _P, _P]),
-    "tq_tq1_transcode_min_m": (_I, []),
+    "tq_tq1_transcode_min_m": (_I64, [_I64, _I64]),
     "tq_gemm_tq1_ws": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
     "tq_gemm_tq1_tiled": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_pack_dev_workspace_bytes": (_I64, [_I64, _I64]),
@@ -249,9 +249,11 @@ def tq_gemm_tq2_bwd_x(dY, qs, scales, dX=None, stream=None):
     return dX
 
 
-def tq_tq1_transcode_min_m() -> int:
-    """Activation rows from which tq_gemm_tq1_ws transcodes to TQ2."""
-    return int(lib.tq_tq1_transcode_min_m())
+def tq_tq1_transcode_min_m(N: int, K: int) -> int:
+    """Activation rows from which tq_gemm_tq1_ws transcodes an N x K matrix to TQ2."""
+    r = int(lib.tq_tq1_transcode_min_m(N, K))
+    _check(min(r, 0), "tq_tq1_transcode_min_m")
+    return r
 
 
 def tq_transcode_tq1_tq2(qs1, K: int, qs2=None, stream=None):
@@ -267,8 +269,8 @@ def tq_transcode_tq1_tq2(qs1, K: int, qs2=None, stream=None):
 
 def tq_gemm_tq1_ws(X, qs, scales, workspace, Y=None, stream=None):
     """tq_gemm_tq1 with a workspace (uint8 device tensor of at least N * K / 4
-    bytes): from tq_tq1_transcode_min_m() rows on, the weights are transcoded
-    once into it and the TQ2 kernels run."""
+    bytes): from tq_tq1_transcode_min_m(N, K) rows on, the weights are
+    transcoded once into it and the TQ2 kernels run."""
     M, K = X.shape
     N, ldq = qs.shape
     Y = _out(Y, M, N, X)

@@ -14,9 +14,13 @@ namespace {
 constexpr int64_t kMaxMN = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxBwdN = int64_t(1) << 20;  // 32-bit offsets in 512 rows of dY
-// From this many activation rows on, TQ1 products with a workspace transcode
-// the weights once and run the TQ2 kernels (measured crossover at K = 8192).
-constexpr int64_t kTq1TranscodeMinM = 48;
+// Activation rows from which a TQ1 product with a workspace transcodes the
+// weights once and runs the TQ2 kernels.  The TQ1 kernels cost a step per 16
+// (skinny) or 32 rows (two slices); the transcoding a fixed read and write of
+// the matrix.  Measured at K = 8192: cheaper from 17 rows at N = 8192 (29.5
+// against 35.7 us at M = 24) and from 33 at N = 28672 (74.9 against 98.1 us
+// at M = 40; 64.6 against 58.3 us at M = 32).
+int64_t tq1_transcode_min_m(int64_t N) { return N <= 16384 ? 17 : 33; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -294,7 +298,10 @@ int tq_transcode_tq1_tq2(const void* qs1, int64_t ldq, int64_t N, int64_t K, voi
   return finish(tq::launch_tq1_to_tq2(qs1, ldq, N, K, qs2, static_cast<hipStream_t>(stream)));
 }
 
-int tq_tq1_transcode_min_m(void) { return (int)kTq1TranscodeMinM; }
+int64_t tq_tq1_transcode_min_m(int64_t N, int64_t K) {
+  if (N < 1 || K < 256 || K % 256) return TQ_ERR_SHAPE;
+  return tq1_transcode_min_m(N);
+}
 
 int tq_gemm_tq1_ws(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,
                    int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
@@ -304,7 +311,8 @@ int tq_gemm_tq1_ws(const void* X, const void* qs, int64_t ldq, const void* scale
   if (st != TQ_OK || noop) return st;
   if (workspace_bytes < 0) return TQ_ERR_SHAPE;
   if (workspace && !aligned16(workspace)) return TQ_ERR_ALIGN;
-  const bool transcode = M >= kTq1TranscodeMinM && workspace && workspace_bytes >= N * (K / 4);
+  const bool transcode =
+      M >= tq1_transcode_min_m(N) && workspace && workspace_bytes >= N * (K / 4);
   if (!transcode) return tq_gemm_tq1_ex(X, qs, ldq, scales, Y, M, N, K, TQ_PATH_AUTO, stream);
   st = device_ready();
   if (st != TQ_OK) return st;

@@ -234,11 +234,13 @@ int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales_f16, vo
 int tq_transcode_tq1_tq2(const void* qs1, int64_t ldq, int64_t N, int64_t K, void* qs2,
                          void* stream);
 
-/* Activation rows from which tq_gemm_tq1_ws transcodes (48). */
-int tq_tq1_transcode_min_m(void);
+/* Activation rows from which tq_gemm_tq1_ws transcodes for an N x K matrix
+ * (the measured crossover: 17 for N <= 16384, else 33); TQ_ERR_SHAPE for
+ * N < 1 or K not a positive multiple of 256. */
+int64_t tq_tq1_transcode_min_m(int64_t N, int64_t K);
 
 /* TQ1 product with a caller workspace, for batch and prefill sizes: with
- * M >= tq_tq1_transcode_min_m() and workspace_bytes >= tq_tq2_bytes(N, K),
+ * M >= tq_tq1_transcode_min_m(N, K) and workspace_bytes >= tq_tq2_bytes(N, K),
  * the weights are first re-packed into the workspace as by
  * tq_transcode_tq1_tq2 and the TQ2 kernels of tq_gemm_tq2 run on it (the
  * TQ1 kernels decode every weight once per activation tile; this decodes it

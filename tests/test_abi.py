@@ -253,7 +253,10 @@ def test_transcode_argument_errors():
 
 
 def test_gemm_tq1_ws_argument_errors():
-    assert tq.tq_tq1_transcode_min_m() == 48
+    assert tq.tq_tq1_transcode_min_m(8192, 8192) == 17
+    assert tq.tq_tq1_transcode_min_m(28672, 8192) == 33
+    assert tq.raw_call("tq_tq1_transcode_min_m", 0, 8192) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_tq1_transcode_min_m", 16, 300) == tq.TQ_ERR_SHAPE
     call = lambda ws=A, nb=1 << 20, M=64, X=A: tq.raw_call(
         "tq_gemm_tq1_ws", X, A, 64, A, A, M, 16, 256, ws, nb, None)
     assert call(M=0, X=None) == tq.TQ_OK

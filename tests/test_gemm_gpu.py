@@ -521,22 +521,24 @@ def test_transcode_matches_host_packer(N, K, ldq):
     np.testing.assert_array_equal(q2.cpu().numpy(), pack("tq2", T))
 
 
-@pytest.mark.parametrize("M", [47, 48, 64, 130])
-def test_gemm_tq1_ws(M):
-    """From 48 rows on the workspace product equals tq_gemm_tq2 on the same
-    trits bit for bit; below, it equals tq_gemm_tq1; both match the oracle."""
-    N, K = 200, 1024
+@pytest.mark.parametrize("M,N", [(16, 200), (17, 200), (64, 200), (130, 200), (32, 16392),
+                                 (33, 16392)])
+def test_gemm_tq1_ws(M, N):
+    """From tq_tq1_transcode_min_m(N, K) rows on the workspace product equals
+    tq_gemm_tq2 on the same trits bit for bit; below, it equals tq_gemm_tq1;
+    both match the oracle (both sides of both switch points)."""
+    K = 1024
     T, s = iid_problem(N, K, 0.31, 92)
     X = activations(M, K, 93)
     ws = torch.empty(N * K // 4 + 64, dtype=torch.uint8, device="cuda")
-    say(f"[tq1 ws] M={M}")
+    say(f"[tq1 ws] M={M} N={N}")
     Y = tq.tq_gemm_tq1_ws(dev(X), dev(pack("tq1", T)), dev(s), ws).cpu().numpy()
-    if M >= tq.tq_tq1_transcode_min_m():
+    if M >= tq.tq_tq1_transcode_min_m(N, K):
         Y2 = tq.tq_gemm_tq2(dev(X), dev(pack("tq2", T)), dev(s)).cpu().numpy()
     else:
         Y2 = tq.tq_gemm_tq1(dev(X), dev(pack("tq1", T)), dev(s)).cpu().numpy()
     np.testing.assert_array_equal(Y.view(np.uint16), Y2.view(np.uint16))
-    check_close(Y, ref(X, T, s), f"tq1 ws M={M}")
+    check_close(Y, ref(X, T, s), f"tq1 ws M={M} N={N}")
 
 
 def test_gemm_tq1_ws_small_workspace_runs_tq1():
