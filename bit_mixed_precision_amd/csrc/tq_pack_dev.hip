@@ -12,13 +12,16 @@
 //
 // Four kernels on one stream, no host round trip:
 //  * tq_abs_sum_kernel: every workgroup adds the 24-bit significands of its
-//    elements into 256 per-exponent 64-bit buckets in LDS, then adds each
+//    elements into 256 per-exponent 64-bit buckets in LDS (four copies per
+//    wave, so that lanes sharing an exponent seldom share an address), then adds each
 //    bucket into a 128-bit total in the workspace (64-bit integer atomics, the
 //    carry counted in the high word); integer sums do not depend on the order,
 //    so the total is the same on every run (a small kernel zeroes it first);
-//  * tq_gamma_kernel: one workgroup shifts the 255 totals into a 384-bit
-//    integer, rounds it to fp64 (nearest, ties to even), forms gamma and its
-//    fp16 bits, and a status (TQ_ERR_VALUE for a non-finite latent or gamma);
+//  * tq_gamma_kernel: one workgroup adds the 32-bit pieces of the 255 shifted
+//    totals into the 12 column sums of a 384-bit integer (LDS integer
+//    atomics, order-free), one thread carries and rounds it to fp64 (nearest,
+//    ties to even), forms gamma and its fp16 bits, and a status
+//    (TQ_ERR_VALUE for a non-finite latent or gamma);
 //  * tq_pack_tq2_dev_kernel / tq_pack_tq1_dev_kernel: one output dword (16
 //    weights) or one TQ1 byte (5 weights) per thread, grid-stride.
 
@@ -63,40 +66,56 @@ __global__ void tq_sum_init_kernel(unsigned long long* lo, unsigned long long* h
   if (e == 0) *bad = 0;
 }
 
+// Four copies of the 256 buckets per wave, picked by lane % 4: latents
+// concentrate on a few exponents, and lanes adding to one LDS address in the
+// same instruction are serialized.  A copy's stride of 260 entries puts the
+// copies of a bucket in different banks.  Each thread keeps four 16-byte
+// loads in flight.
+constexpr int kCopies = 4;
+constexpr int kCopyStride = 260;
+constexpr int kSumUnroll = 4;
+
 __global__ __launch_bounds__(kSumThreads) void tq_abs_sum_kernel(const float* __restrict__ W,
                                                                  int64_t total,
                                                                  unsigned long long* lo,
                                                                  unsigned long long* hi,
                                                                  int* bad_out) {
-  __shared__ unsigned long long bk[kSumWaves][256];
+  __shared__ unsigned long long bk[kSumWaves * kCopies * kCopyStride];
   __shared__ int bad;
-  for (int i = threadIdx.x; i < kSumWaves * 256; i += blockDim.x) (&bk[0][0])[i] = 0ull;
+  for (int i = threadIdx.x; i < kSumWaves * kCopies * kCopyStride; i += blockDim.x) bk[i] = 0ull;
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
-  const int wave = threadIdx.x >> 6;
+  unsigned long long* mine =
+      bk + ((threadIdx.x >> 6) * kCopies + (threadIdx.x & (kCopies - 1))) * kCopyStride;
   int my_bad = 0;
   const int64_t q4 = total / 4;  // total is a multiple of 256
   const float4* W4 = reinterpret_cast<const float4*>(W);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < q4;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const float4 v = W4[i];
-    const float vs[4] = {v.x, v.y, v.z, v.w};
+       i += kSumUnroll * stride) {
+    float4 v[kSumUnroll];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t u = __float_as_uint(vs[t]);
-      const uint32_t e = (u >> 23) & 0xFFu;
-      uint32_t m = u & 0x7FFFFFu;
-      if (e == 0xFFu) my_bad = 1;
-      if (e) m |= 0x800000u;
-      atomicAdd(&bk[wave][e], (unsigned long long)m);
+    for (int r = 0; r < kSumUnroll; ++r)
+      v[r] = i + r * stride < q4 ? W4[i + r * stride] : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < kSumUnroll; ++r) {
+      const float vs[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t u = __float_as_uint(vs[t]);
+        const uint32_t e = (u >> 23) & 0xFFu;
+        uint32_t m = u & 0x7FFFFFu;
+        if (e == 0xFFu) my_bad = 1;
+        if (e) m |= 0x800000u;
+        if (m) atomicAdd(&mine[e], (unsigned long long)m);
+      }
     }
   }
   if (my_bad) atomicOr(&bad, 1);
   __syncthreads();
   for (int e = threadIdx.x; e < 256; e += blockDim.x) {
     unsigned long long s = 0;
-#pragma unroll
-    for (int w = 0; w < kSumWaves; ++w) s += bk[w][e];  // < 2^58: no overflow
+    for (int c = 0; c < kSumWaves * kCopies; ++c) s += bk[c * kCopyStride + e];  // < 2^58
     if (s) {
       const unsigned long long old = atomicAdd(&lo[e], s);
       if (old + s < old) atomicAdd(&hi[e], 1ull);  // this add carried out of 64 bits
@@ -105,62 +124,58 @@ __global__ __launch_bounds__(kSumThreads) void tq_abs_sum_kernel(const float* __
   if (threadIdx.x == 0 && bad) atomicOr(bad_out, 1);
 }
 
-// 384-bit unsigned integer in 32-bit limbs (single-thread use).
-struct BigSum {
-  static constexpr int kLimbs = 12;
-  uint32_t limb[kLimbs];
-  __device__ void clear() {
-    for (int i = 0; i < kLimbs; ++i) limb[i] = 0;
-  }
-  __device__ void add_shifted(uint64_t v, int shift) {  // += v << shift
-    int li = shift / 32, bi = shift % 32;
-    uint32_t part[3];
-    part[0] = (uint32_t)(v << bi);
-    part[1] = (uint32_t)(bi ? (v >> (32 - bi)) : (v >> 32));
-    part[2] = (uint32_t)(bi ? (v >> (64 - bi)) : 0);
-    uint64_t carry = 0;
-    for (int i = li; i < kLimbs; ++i) {
-      const uint64_t p = i - li < 3 ? part[i - li] : 0;
-      const uint64_t s = (uint64_t)limb[i] + p + carry;
-      limb[i] = (uint32_t)s;
-      carry = s >> 32;
-      if (i - li >= 2 && carry == 0) break;
+// The exact total as a 384-bit integer: 12 column sums of 32-bit pieces
+// (each column below 2^41, so 64-bit), then carries.  Every index is a
+// compile-time constant so that the limbs stay in registers.
+constexpr int kLimbs = 12;
+
+// col[li..li+2] += the 32-bit pieces of v << shift (shift <= 317).
+__device__ __forceinline__ void add_pieces(unsigned long long* col, unsigned long long v,
+                                           int shift) {
+  if (!v) return;
+  const int li = shift >> 5;
+  const int bi = shift & 31;
+  const uint32_t p0 = (uint32_t)(v << bi);
+  const uint32_t p1 = (uint32_t)(bi ? v >> (32 - bi) : v >> 32);
+  const uint32_t p2 = (uint32_t)(bi ? v >> (64 - bi) : 0ull);
+  if (p0) atomicAdd(&col[li], (unsigned long long)p0);
+  if (p1) atomicAdd(&col[li + 1], (unsigned long long)p1);
+  if (p2) atomicAdd(&col[li + 2], (unsigned long long)p2);
+}
+
+// L (little-endian 32-bit limbs) * 2^scale_exp, rounded to the nearest fp64,
+// ties to even: a 64-bit window under the top bit gives the 53-bit
+// significand, its next bit the guard, the rest of the window and every bit
+// below it the sticky bit.
+__device__ double limbs_to_double(const uint32_t (&L)[kLimbs], int scale_exp) {
+  int h = -1;
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i)
+    if (L[i]) h = 32 * i + 31 - __clz(L[i]);
+  if (h < 0) return 0.0;
+  const int lo = h - 63;  // bit of the value at bit 0 of the window
+  uint64_t W = 0;
+  bool sticky = false;
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) {
+    const int off = 32 * i - lo;  // window position of the limb's bit 0
+    const uint64_t v = L[i];
+    if (off >= 64) continue;
+    if (off >= 0) {
+      W |= v << off;
+    } else if (off > -32) {
+      W |= v >> (-off);
+      sticky |= (v & ((uint64_t(1) << (-off)) - 1)) != 0;
+    } else {
+      sticky |= v != 0;
     }
   }
-  __device__ int top_bit() const {
-    for (int i = kLimbs - 1; i >= 0; --i)
-      if (limb[i]) return i * 32 + 31 - __clz(limb[i]);
-    return -1;
-  }
-  __device__ int bit(int b) const { return b < 0 ? 0 : (limb[b / 32] >> (b % 32)) & 1; }
-  __device__ bool any_below(int b) const {
-    if (b <= 0) return false;
-    const int full = b / 32;
-    for (int i = 0; i < full; ++i)
-      if (limb[i]) return true;
-    const int rem = b % 32;
-    return rem && (limb[full] & ((1u << rem) - 1));
-  }
-  // value * 2^scale_exp rounded to nearest even fp64
-  __device__ double to_double(int scale_exp) const {
-    const int h = top_bit();
-    if (h < 0) return 0.0;
-    uint64_t mant = 0;
-    int lo = h - 52;
-    for (int b = h; b >= (lo > 0 ? lo : 0); --b) mant = (mant << 1) | (uint64_t)bit(b);
-    if (lo < 0) return ldexp((double)mant, scale_exp);
-    const int guard = bit(lo - 1);
-    const bool sticky = any_below(lo - 1);
-    if (guard && (sticky || (mant & 1))) {
-      ++mant;
-      if (mant == (uint64_t(1) << 53)) {
-        mant >>= 1;
-        ++lo;
-      }
-    }
-    return ldexp((double)mant, lo + scale_exp);
-  }
-};
+  uint64_t mant = W >> 11;
+  const bool guard = (W >> 10) & 1;
+  sticky |= (W & 0x3FFu) != 0;
+  if (guard && (sticky || (mant & 1))) ++mant;  // 2^53 is exact in the ldexp below
+  return ldexp((double)mant, h - 52 + scale_exp);
+}
 
 // One round-to-nearest-even step from binary64 to binary16.
 __device__ uint16_t f64_to_f16_bits_dev(double x) {
@@ -189,20 +204,31 @@ __device__ uint16_t f64_to_f16_bits_dev(double x) {
   return sign | (uint16_t)r;
 }
 
-__global__ __launch_bounds__(64) void tq_gamma_kernel(const unsigned long long* lo,
-                                                      const unsigned long long* hi,
-                                                      const int* bad, int64_t total, double eps,
-                                                      Info* info, double* gamma_out,
-                                                      int* status_out) {
-  if (threadIdx.x != 0) return;
-  BigSum s;
-  s.clear();
-  for (int e = 0; e < 255; ++e) {
+__global__ __launch_bounds__(256) void tq_gamma_kernel(const unsigned long long* lo,
+                                                       const unsigned long long* hi,
+                                                       const int* bad, int64_t total, double eps,
+                                                       Info* info, double* gamma_out,
+                                                       int* status_out) {
+  __shared__ unsigned long long col[kLimbs];
+  if (threadIdx.x < kLimbs) col[threadIdx.x] = 0;
+  __syncthreads();
+  const int e = threadIdx.x;
+  if (e < 255) {
     const int shift = (e ? e : 1) - 1;  // m * 2^(e' - 150) = m * 2^(e' - 1) * 2^-149
-    if (lo[e]) s.add_shifted(lo[e], shift);
-    if (hi[e]) s.add_shifted(hi[e], shift + 64);
+    add_pieces(col, lo[e], shift);
+    add_pieces(col, hi[e], shift + 64);
   }
-  const double S = s.to_double(-149);
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  uint32_t L[kLimbs];
+  unsigned long long carry = 0;
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) {
+    const unsigned long long t = col[i] + carry;
+    L[i] = (uint32_t)t;
+    carry = t >> 32;
+  }
+  const double S = limbs_to_double(L, -149);
   const double g = eps + S / (double)total;
   const bool ok = !*bad && isfinite(g) && g > 0.0;
   info->gamma = g;
@@ -311,7 +337,7 @@ int launch_gamma(const float* W, int64_t N, int64_t K, double eps, double* gamma
   hipLaunchKernelGGL(tq_sum_init_kernel, dim3(1), dim3(256), 0, stream, lo, hi, bad);
   hipLaunchKernelGGL(tq_abs_sum_kernel, dim3((unsigned)sum_groups(N, K)), dim3(kSumThreads), 0,
                      stream, W, N * K, lo, hi, bad);
-  hipLaunchKernelGGL(tq_gamma_kernel, dim3(1), dim3(64), 0, stream, lo, hi, bad, N * K, eps,
+  hipLaunchKernelGGL(tq_gamma_kernel, dim3(1), dim3(256), 0, stream, lo, hi, bad, N * K, eps,
                      info, gamma, status);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }

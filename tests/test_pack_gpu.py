@@ -42,7 +42,7 @@ def host_pack(fmt, W, eps, ldq=None):
 
 @pytest.mark.parametrize("fmt", [2, 1])
 @pytest.mark.parametrize("N,K,ldq", [(1, 256, None), (37, 512, None), (100, 1024, 240),
-                                     (777, 2560, None), (4096, 8192, None)])
+                                     (100, 1024, 237), (777, 2560, None), (4096, 8192, None)])
 def test_device_pack_matches_host(fmt, N, K, ldq):
     say(f"[pack] fmt={fmt} N={N} K={K} ldq={ldq}")
     W = latent_weights_f32(seed_for(80, N, K), N, K)
