@@ -20,7 +20,8 @@
 // 16-byte load; each byte's five fields (10 bits) come from a 256-entry table
 // that every workgroup builds in LDS with the multiply-by-3 decoder (t = 3 q,
 // digit = t >> 8, q = t & 255, five times) and are OR-ed into the unit's
-// 160-bit output (byte i at bit 10 i), written as five dwords.
+// 160-bit output (byte i at bit 10 i); the workgroup's contiguous output is
+// staged in LDS and written with consecutive lanes on consecutive dwords.
 
 #include "tq_common.h"
 #include "tq_kernels.h"
@@ -35,6 +36,7 @@ __global__ __launch_bounds__(kTcThreads) void tq1_to_tq2_kernel(const uint8_t* _
                                                                int ldq, int units, int64_t total,
                                                                int K, uint8_t* __restrict__ qs2) {
   __shared__ uint32_t table[256];
+  __shared__ uint32_t stage[5 * kTcThreads];
   {
     // fields of byte value threadIdx.x: digits of the multiply-by-3 decoder
     uint32_t q = threadIdx.x, f = 0;
@@ -47,24 +49,40 @@ __global__ __launch_bounds__(kTcThreads) void tq1_to_tq2_kernel(const uint8_t* _
     table[threadIdx.x] = f;
   }
   __syncthreads();
-  const int64_t t = (int64_t)blockIdx.x * kTcThreads + threadIdx.x;
-  if (t >= total) return;
-  const int64_t n = t / units;
-  const int u = (int)(t - n * units);
-  const u32x4 raw = *reinterpret_cast<const u32x4*>(qs1 + n * ldq + 16 * u);
-  uint32_t out[5] = {0u, 0u, 0u, 0u, 0u};
+  // The workgroup's units are consecutive, and so is their output: TQ2 dword
+  // (n K / 16 + 5 u + w) for unit u of row n (a row's last unit may hold
+  // fewer than five).  Stage it in LDS, then write it with consecutive lanes
+  // on consecutive dwords.
+  const int64_t t0 = (int64_t)blockIdx.x * kTcThreads;
+  const int64_t t = t0 + threadIdx.x;
+  const int64_t n0 = t0 / units;
+  const int64_t base = n0 * (K >> 4) + 5 * (t0 - n0 * units);  // first dword of the workgroup
+  if (t < total) {
+    const int64_t n = t / units;
+    const int u = (int)(t - n * units);
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(qs1 + n * ldq + 16 * u);
+    uint32_t out[5] = {0u, 0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const uint32_t f = table[(raw[i >> 2] >> (8 * (i & 3))) & 0xFFu];
-    const int pos = 10 * i;
-    out[pos >> 5] |= f << (pos & 31);
-    if ((pos & 31) > 22) out[(pos >> 5) + 1] |= f >> (32 - (pos & 31));
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t f = table[(raw[i >> 2] >> (8 * (i & 3))) & 0xFFu];
+      const int pos = 10 * i;
+      out[pos >> 5] |= f << (pos & 31);
+      if ((pos & 31) > 22) out[(pos >> 5) + 1] |= f >> (32 - (pos & 31));
+    }
+    const int local = (int)(n * (K >> 4) + 5 * u - base);
+    const int k0 = 80 * u;
+#pragma unroll
+    for (int w = 0; w < 5; ++w)
+      if (k0 + 16 * w < K) stage[local + w] = out[w];
   }
-  uint32_t* dst = reinterpret_cast<uint32_t*>(qs2 + n * (K >> 2) + 20 * u);
-  const int k0 = 80 * u;
-#pragma unroll
-  for (int w = 0; w < 5; ++w)
-    if (k0 + 16 * w < K) dst[w] = out[w];
+  __syncthreads();
+  const int64_t tl = (t0 + kTcThreads < total ? t0 + kTcThreads : total) - 1;  // last unit
+  const int64_t nl = tl / units;
+  const int ul = (int)(tl - nl * units);
+  const int rem = (K - 80 * ul) >> 4;  // dwords of the last unit
+  const int count = (int)(nl * (K >> 4) + 5 * ul + (rem < 5 ? rem : 5) - base);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(qs2) + base;
+  for (int i = threadIdx.x; i < count; i += kTcThreads) dst[i] = stage[i];
 }
 
 }  // namespace
