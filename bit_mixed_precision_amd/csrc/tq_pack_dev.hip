@@ -22,8 +22,9 @@
 //    atomics, order-free), one thread carries and rounds it to fp64 (nearest,
 //    ties to even), forms gamma and its fp16 bits, and a status
 //    (TQ_ERR_VALUE for a non-finite latent or gamma);
-//  * tq_pack_tq2_dev_kernel / tq_pack_tq1_dev_kernel: one output dword (16
-//    weights) or one TQ1 byte (5 weights) per thread, grid-stride.
+//  * tq_pack_tq2_dev_kernel: one output dword (16 weights) per thread,
+//    grid-stride; tq_pack_tq1_dev_kernel: 1024 TQ1 bytes of a row per
+//    workgroup, their latents staged in LDS by coalesced loads.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -271,35 +272,52 @@ __global__ __launch_bounds__(256) void tq_pack_tq2_dev_kernel(const float* __res
   }
 }
 
-// One TQ1 byte per thread: group g of row n holds weights 5 g .. 5 g + 4, the
-// first as the most significant base-3 digit, weights past K as zero trits;
-// bytes g >= ceil(K / 5) of the row are 0.
+// TQ1 bytes of one row, 1024 at a time per workgroup of 256 threads: the
+// chunk's 5120 latents (weights 5 g .. 5 g + 4 of its groups g) come into LDS
+// with coalesced 16-byte loads (zero past K), then thread t encodes groups
+// t, t + 256, t + 512, t + 768 from LDS (a stride of 5 dwords, so the 64
+// lanes hit 64 banks) and consecutive lanes write consecutive bytes.  Group g
+// holds weights 5 g .. 5 g + 4, the first as the most significant base-3
+// digit, weights past K as zero trits; bytes g >= ceil(K / 5) of the row are 0.
+constexpr int kTq1Chunk = 1024;  // groups per workgroup
 __global__ __launch_bounds__(256) void tq_pack_tq1_dev_kernel(const float* __restrict__ W,
                                                               int64_t N, int64_t K, int64_t ldq,
                                                               const Info* info,
                                                               uint8_t* __restrict__ qs,
                                                               uint16_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) float lat[5 * kTq1Chunk];
   const double gamma = info->gamma;
   const uint16_t h = (uint16_t)info->h;
   const int64_t G = (K + 4) / 5;
-  const int64_t bytes = N * ldq;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < bytes;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t n = i / ldq;
-    const int64_t g = i - n * ldq;
-    uint8_t b = 0;
-    if (g < G) {
-      const float* row = W + n * K;
-      unsigned code = 0;
+  const int64_t chunks = (ldq + kTq1Chunk - 1) / kTq1Chunk;
+  for (int64_t wg = blockIdx.x; wg < N * chunks; wg += gridDim.x) {
+    const int64_t n = wg / chunks;
+    const int64_t g0 = (wg - n * chunks) * kTq1Chunk;
+    const int64_t k0 = 5 * g0;
+    __syncthreads();  // the previous chunk's reads are done
 #pragma unroll
-      for (int j = 0; j < 5; ++j) {
-        const int64_t k = 5 * g + j;
-        const int t = k < K ? trit_of(row[k], gamma) : 0;
-        code = 3 * code + (unsigned)(t + 1);
-      }
-      b = (uint8_t)((code * 256 + 242) / 243);
+    for (int r = 0; r < 5; ++r) {
+      const int q = threadIdx.x + 256 * r;  // float4 index in the chunk
+      const int64_t k = k0 + 4 * q;        // K % 4 == 0: all in the row or all past it
+      const float4 v = k < K ? *reinterpret_cast<const float4*>(W + n * K + k)
+                             : float4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<float4*>(lat + 4 * q) = v;
     }
-    qs[i] = b;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = threadIdx.x + 256 * j;  // group in the chunk
+      const int64_t g = g0 + c;
+      if (g >= ldq) continue;
+      uint32_t b = 0;
+      if (g < G) {
+        unsigned code = 0;
+#pragma unroll
+        for (int e = 0; e < 5; ++e) code = 3 * code + (unsigned)(trit_of(lat[5 * c + e], gamma) + 1);
+        b = (code * 256 + 242) / 243;
+      }
+      qs[n * ldq + g] = (uint8_t)b;
+    }
   }
   const int64_t ns = N * (K / 256);
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < ns;
@@ -382,8 +400,9 @@ int tq_pack_tq1_dev(const float* W, int64_t N, int64_t K, double eps, int64_t ld
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   st = launch_gamma(W, N, K, eps, gamma, status, ws, s);
   if (st != TQ_OK) return st;
-  hipLaunchKernelGGL(tq_pack_tq1_dev_kernel, dim3(pack_grid(N * ldq)), dim3(256), 0, s, W, N, K,
-                     ldq, reinterpret_cast<const Info*>(ws), qs, scales);
+  const int64_t chunks = N * ((ldq + kTq1Chunk - 1) / kTq1Chunk);
+  hipLaunchKernelGGL(tq_pack_tq1_dev_kernel, dim3((unsigned)(chunks < 65536 ? chunks : 65536)),
+                     dim3(256), 0, s, W, N, K, ldq, reinterpret_cast<const Info*>(ws), qs, scales);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
