@@ -247,8 +247,9 @@ int64_t tq_tq1_transcode_min_m(int64_t N, int64_t K);
  * once per call), so Y equals tq_gemm_tq2's on the same trits bit for bit.
  * Otherwise (smaller M, no or too small a workspace) it is tq_gemm_tq1.
  * The workspace is device memory owned by the caller, 16-byte aligned when
- * given (TQ_ERR_ALIGN otherwise), overwritten by the call; calls that
- * overlap on one workspace race.  Everything else is as tq_gemm_tq1. */
+ * given (TQ_ERR_ALIGN otherwise), overwritten by the call, and must not
+ * overlap X, qs, scales or Y; calls that overlap on one workspace race.
+ * Everything else is as tq_gemm_tq1. */
 int tq_gemm_tq1_ws(const void* X, const void* qs, int64_t ldq, const void* scales_f16, void* Y,
                    int64_t M, int64_t N, int64_t K, void* workspace, int64_t workspace_bytes,
                    void* stream);
