@@ -207,7 +207,11 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   const int ns_all = GLU ? 2 * ns : ns;
   const uint16_t* ssrc = scales + (size_t)n_base * nb;
   const uint16_t* ssrc2 = GLU ? scales2 + (size_t)n_base * nb : ssrc;
-  const int sc_off = up ? ns : 0;
+  // Staged scale rows sit nb + 1 floats apart, so the 16 rows a wave reads
+  // at once fall in 16 different LDS banks (nb apart, with nb a multiple of
+  // 32 or 64 as it usually is, they would all share one bank).
+  const int sc_row = ((up ? rows : 0) + nrow) * (nb + 1);
+  const float inv_nb = __builtin_amdgcn_rcpf((float)nb);  // within 1 ulp: ample for the row index
 
   float4v acc = {0.f, 0.f, 0.f, 0.f};
   u32x4 wbuf[D];
@@ -221,7 +225,7 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   auto compute = [&](int d, int b, int bw) {
     const u32x4 w = wbuf[d];
     const u32x4 w8 = shift8(w);
-    const float sc = STAGE ? sc_lds[sc_off + nrow * nb + b] : h2f(sbuf[d]);
+    const float sc = STAGE ? sc_lds[sc_row + b] : h2f(sbuf[d]);
     float4v c0 = *reinterpret_cast<const float4v*>(ba + 16 * bw);  // -2^-24 (row sums)
     float4v c1 = {0.f, 0.f, 0.f, 0.f};
     const unsigned char* xb = xa + bw * 512;
@@ -294,7 +298,10 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
 #pragma unroll
           for (int r = 0; r < kScaleRegs; ++r) {
             const int e = threadIdx.x + r * T;
-            if (e < ns_all) sc_lds[e] = h2f(sreg[r]);
+            // row of scale e: exact in fp32, since e < 2^14 keeps the rounding
+            // error far below the 0.5 / nb margin to the nearest integer
+            const int row = (int)(((float)e + 0.5f) * inv_nb);
+            if (e < ns_all) sc_lds[e + row] = h2f(sreg[r]);
           }
         }
       }
@@ -376,7 +383,8 @@ hipError_t launch_tq2_skinny_s(const GemmArgs& a, const void* qs2, const void* s
   return hipGetLastError();
 }
 
-int64_t scale_lds_bytes(int64_t RG, int64_t K) { return ((16 * RG * (K / 256) * 4) + 15) & ~15; }
+// Staged scales: 16 RG rows of K / 256 floats, rows padded by one float.
+int64_t scale_lds_bytes(int64_t RG, int64_t K) { return ((16 * RG * (K / 256 + 1) * 4) + 15) & ~15; }
 
 }  // namespace
 

@@ -193,6 +193,10 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
   const uint8_t* wrow = qs + (size_t)(n_base + nrow) * ldq + 8 * g;
   const uint16_t* srow_g = scales + (size_t)(n_base + nrow) * nb;
   const int ns = STAGE ? rows * nb : 0;
+  // Staged scale rows sit nb + 1 floats apart: the 16 rows a wave reads at
+  // once then fall in 16 different LDS banks.
+  const int sc_row = nrow * (nb + 1);
+  const float inv_nb = __builtin_amdgcn_rcpf((float)nb);  // within 1 ulp: ample for the row index
   const uint16_t* ssrc = scales + (size_t)n_base * nb;
   // Activation row of this lane in slice ms (rows past M repeat the last one;
   // their results are never written).
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     __builtin_amdgcn_sched_barrier(0);
   };
   auto scale_at = [&](int b) -> float {
-    if constexpr (STAGE) return sc_lds[nrow * nb + b];
+    if constexpr (STAGE) return sc_lds[sc_row + b];
     return h2f(srow_g[b]);
   };
   auto compute = [&](int d, int u, int uw) {
@@ -306,7 +310,9 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
           const int e = threadIdx.x + r * T;
           uint32_t v = sreg[r];
           asm volatile("" : "+v"(v));  // convert here, not ahead of the loop (no early wait)
-          if (e < ns) sc_lds[e] = h2f((uint16_t)v);
+          // row of scale e: exact in fp32 (e < 2^14, far below the margin)
+          const int row = (int)(((float)e + 0.5f) * inv_nb);
+          if (e < ns) sc_lds[e + row] = h2f((uint16_t)v);
         }
       }
     }
@@ -391,7 +397,8 @@ hipError_t launch_tq1_ms(int ms, const GemmArgs& a, hipStream_t stream, dim3 gri
   return launch_tq1_s<STAGE, 1>(a, stream, grid, W, lds, RG, lwk, nuw, xregion);
 }
 
-int64_t tq1_scale_bytes(int64_t RG, int64_t K) { return ((16 * RG * (K / 256) * 4) + 15) & ~15; }
+// Staged scales: 16 RG rows of K / 256 floats, rows padded by one float.
+int64_t tq1_scale_bytes(int64_t RG, int64_t K) { return ((16 * RG * (K / 256 + 1) * 4) + 15) & ~15; }
 
 }  // namespace
 
