@@ -100,7 +100,7 @@ def test_tile_errors():
     assert _gt4(2, 2, 1, 4, X=None) == tq.TQ_ERR_NULL
     assert _gt4(2, 2, 1, 4, K=300) == tq.TQ_ERR_SHAPE
     for tile in [(2, 2, 4, 2), (2, 2, 2, 2), (2, 3, 1, 4), (8, 4, 4, 2), (4, 1, 1, 4),
-                 (3, 2, 1, 4), (2, 2, 1, 8)]:
+                 (3, 2, 1, 4), (4, 2, 1, 8), (2, 4, 1, 8)]:
         assert _gt4(*tile) == tq.TQ_ERR_UNSUPPORTED, tile
     assert _gt4(3, 2, 1, 4, X=None, M=0) == tq.TQ_OK
 
