@@ -460,11 +460,12 @@ hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
 // when 64 would leave compute units idle (M <= 32: 18.4 against 23.1 us at
 // N = 8192); past M = 64 the 8-wave 64 x 64 tile (2 row groups of 32 x 4
 // k-groups: 32.0 against 34.6 us at N = 8192, M = 128).  When the 32 x 32
-// tiles number no more than the compute units (N <= 8192 on 256 CUs), they
-// run as 8 k-groups of one wave each instead of 4, twice the waves per SIMD
-// on the same workgroups (M = 32, N = 8192: 16.6 against 18.4 us; M = 17:
-// 15.7 against 18.0 us); with more tiles than compute units the 8-wave
-// workgroup (one per CU) needs two passes and loses.
+// or 32 x 64 tiles number no more than the compute units (N <= 8192 on 256
+// CUs), they run as 8 k-groups of one wave each instead of 4, twice the
+// waves per SIMD on the same workgroups (M = 32, N = 8192: 16.6 against
+// 18.4 us; M = 17: 15.7 against 18.0 us; M = 64: 22.8 against 23.9 us);
+// with more tiles than compute units the 8-wave workgroup (one per CU)
+// needs two passes and loses.
 TiledShape tiled_shape(int64_t M, int64_t N) {
   const int64_t cus = device_cus();
   auto fills = [&](const TiledShape& t) {
@@ -477,7 +478,11 @@ TiledShape tiled_shape(int64_t M, int64_t N) {
     const bool wide = M > 64;
     const TiledShape t8 = wide ? TiledShape{8, 2, 4, 2} : TiledShape{4, 4, 2, 4};
     if (fills(t8)) return t8;
-    return wide ? TiledShape{4, 2, 2, 4} : TiledShape{2, 4, 1, 4};
+    if (wide) return TiledShape{4, 2, 2, 4};
+    // 32 x 64 tiles as 8 one-wave k-groups when they fit one per CU (M = 64,
+    // N = 8192: 22.8 against 23.9 us; M = 33: 21.8 against 23.5 us)
+    const int64_t wgs = ((N + 63) / 64) * ((M + 31) / 32);
+    return wgs <= cus ? TiledShape{2, 4, 1, 8} : TiledShape{2, 4, 1, 4};
   }
   const TiledShape t{2, 4, 1, 4};
   if (fills(t)) return t;
@@ -488,7 +493,8 @@ TiledShape tiled_shape(int64_t M, int64_t N) {
 template <int MT>
 hipError_t launch_mt(const TiledShape& t, const GemmArgs& a, hipStream_t stream) {
   if constexpr (MT == 2) {
-    if (t.nr == 2 && t.kg == 8) return launch_tiled<2, 2, 1, 8>(a, stream);
+    if (t.kg == 8) return t.nr == 2 ? launch_tiled<2, 2, 1, 8>(a, stream)
+                                    : launch_tiled<2, 4, 1, 8>(a, stream);
   }
   if (t.nr == 2) return t.ng == 2 ? launch_tiled<MT, 2, 2, 4>(a, stream)
                                   : launch_tiled<MT, 2, 1, 4>(a, stream);
@@ -501,7 +507,7 @@ hipError_t launch_mt(const TiledShape& t, const GemmArgs& a, hipStream_t stream)
 bool tiled_compiled(const TiledShape& t) {
   if (t.mt == 8) return t.nr == 2 && t.ng == 4 && t.kg == 2;
   if (t.mt != 2 && t.mt != 4) return false;
-  if (t.nr == 2 && t.kg == 8) return t.mt == 2 && t.ng == 1;
+  if (t.kg == 8) return t.mt == 2 && t.ng == 1 && (t.nr == 2 || t.nr == 4);
   if (t.nr == 2) return t.kg == 4 && (t.ng == 1 || t.ng == 2);
   if (t.nr != 4) return false;
   return (t.ng == 4 && t.kg == 2) || (t.ng == 2 && t.kg == 4) || (t.ng == 2 && t.kg == 2) ||

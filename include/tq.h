@@ -184,8 +184,9 @@ int tq_pack_tq1_dev(const float* W, int64_t N, int64_t K, double eps, int64_t ld
 /* TQ2 product on the tiled kernel with an explicit tile, for tuning and for
  * tests of every tile: 16 mt activation rows x 64 ng weight rows (32 ng when
  * mt = 8) per workgroup of ng x kg waves (kg of them split K).  Compiled
- * tiles: mt in {2, 4} with (ng, kg) in {(4, 2), (2, 4), (2, 2), (1, 4)}, and
- * mt = 8 with (4, 2); any other tile gives TQ_ERR_UNSUPPORTED.  Everything
+ * tiles: mt in {2, 4} with (ng, kg) in {(4, 2), (2, 4), (2, 2), (1, 4)},
+ * mt = 2 with (1, 8), and mt = 8 with (4, 2); any other tile gives
+ * TQ_ERR_UNSUPPORTED.  Everything
  * else is as tq_gemm_tq2. */
 int tq_gemm_tq2_tiled(const void* X, const void* qs, const void* scales_f16, void* Y,
                       int64_t M, int64_t N, int64_t K, int mt, int ng, int kg, void* stream);
@@ -269,7 +270,8 @@ int tq_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
 /* As tq_gemm_tq2_tiled with the weight rows per wave explicit: 16 mt
  * activation rows x 16 nr ng weight rows per workgroup of ng x kg waves.
  * Compiled tiles (mt, nr, ng, kg): mt in {2, 4} with (4, 4, 2), (4, 2, 4),
- * (4, 2, 2), (4, 1, 4), (2, 1, 4), (2, 2, 4), and (2, 2, 1, 8), (8, 2, 4, 2);
+ * (4, 2, 2), (4, 1, 4), (2, 1, 4), (2, 2, 4), and (2, 2, 1, 8), (2, 4, 1, 8),
+ * (8, 2, 4, 2);
  * any other gives TQ_ERR_UNSUPPORTED.  Everything else is as tq_gemm_tq2. */
 int tq_gemm_tq2_tile(const void* X, const void* qs, const void* scales_f16, void* Y, int64_t M,
                      int64_t N, int64_t K, int mt, int nr, int ng, int kg, void* stream);

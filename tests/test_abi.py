@@ -87,7 +87,7 @@ def test_tiled_tile_errors():
     # argument checks first, then the tile, both before any device work
     assert _gt(4, 2, 2, X=None) == tq.TQ_ERR_NULL
     assert _gt(4, 2, 2, K=300) == tq.TQ_ERR_SHAPE
-    for tile in [(3, 2, 2), (4, 4, 4), (2, 1, 8), (4, 8, 1), (0, 2, 2), (4, 1, 2)]:
+    for tile in [(3, 2, 2), (4, 4, 4), (4, 1, 8), (2, 2, 8), (4, 8, 1), (0, 2, 2), (4, 1, 2)]:
         assert _gt(*tile) == tq.TQ_ERR_UNSUPPORTED, tile
     assert _gt(3, 2, 2, X=None, M=0) == tq.TQ_OK
 
@@ -100,7 +100,7 @@ def test_tile_errors():
     assert _gt4(2, 2, 1, 4, X=None) == tq.TQ_ERR_NULL
     assert _gt4(2, 2, 1, 4, K=300) == tq.TQ_ERR_SHAPE
     for tile in [(2, 2, 4, 2), (2, 2, 2, 2), (2, 3, 1, 4), (8, 4, 4, 2), (4, 1, 1, 4),
-                 (3, 2, 1, 4), (4, 2, 1, 8), (2, 4, 1, 8)]:
+                 (3, 2, 1, 4), (4, 2, 1, 8), (4, 4, 1, 8), (2, 4, 2, 8)]:
         assert _gt4(*tile) == tq.TQ_ERR_UNSUPPORTED, tile
     assert _gt4(3, 2, 1, 4, X=None, M=0) == tq.TQ_OK
 

@@ -106,7 +106,7 @@ def test_small_parity(fmt, path, M, N, K):
 TILES = [(mt, 4, ng, kg) for mt in (2, 4) for ng, kg in ((4, 2), (2, 4), (2, 2), (1, 4))]
 TILES += [(mt, 2, ng, 4) for mt in (2, 4) for ng in (1, 2)]  # 32 weight rows per wave
 TILES.append((8, 2, 4, 2))  # 128 activation rows x 32 weight rows per wave
-TILES.append((2, 2, 1, 8))  # 32 x 32 over 8 k-groups
+TILES += [(2, 2, 1, 8), (2, 4, 1, 8)]  # 32 x 32 and 32 x 64 over 8 k-groups
 # ragged in M and N, K / 256 = 1, 2, 3, 5 (fewer blocks than k-groups, odd counts)
 TILE_SHAPES = [(17, 100, 256), (40, 300, 768), (64, 257, 1024), (100, 520, 1280),
                (130, 1000, 512)]
