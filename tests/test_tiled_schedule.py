@@ -17,13 +17,10 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "bit_mixed_precision_amd", "csrc")
 
-# (MT, NG, KG) of the compiled tiles; NR(MT) weight-row groups of 16 per wave.
-TILES = [(mt, ng, kg) for mt in (2, 4) for ng, kg in ((4, 2), (2, 4), (2, 2), (1, 4))]
-TILES.append((8, 4, 2))
-
-
-def nr_of(mt):
-    return 2 if mt == 8 else 4
+# (MT, NR, NG, KG) of every compiled tile (NR weight-row groups of 16 per wave).
+TILES = [(mt, 4, ng, kg) for mt in (2, 4) for ng, kg in ((4, 2), (2, 4), (2, 2), (1, 4))]
+TILES += [(mt, 2, ng, 4) for mt in (2, 4) for ng in (1, 2)]
+TILES += [(8, 2, 4, 2), (2, 2, 1, 8), (2, 4, 1, 8)]
 
 DRIVER = r"""
 #include <cstdio>
@@ -36,7 +33,7 @@ int main() {
     const int budget = wv == 8 ? 160 * 1024 : 80 * 1024;
     const tq::RingPlan p = tq::ring_plan(stage, round, budget);
     const int kper = kg * 2 * mt / wv;
-    std::printf("%%d %%d %%d %%d %%d %%d", mt, ng, kg, p.xs, p.wd, kper);
+    std::printf("%%d %%d %%d %%d %%d %%d %%d", mt, nr, ng, kg, p.xs, p.wd, kper);
     for (int r0 = 1; r0 >= 0; --r0)
       for (int ch = 0; ch < 4; ++ch)
         std::printf(" %%d", tq::vm_younger(p.xs, kper, nr + 1, ch, r0));
@@ -53,16 +50,16 @@ def plans(tmp_path_factory):
         pytest.skip("g++ not available")
     d = tmp_path_factory.mktemp("sched")
     src = d / "drv.cpp"
-    src.write_text(DRIVER % ", ".join("{%d, %d, %d, %d}" % (*t, nr_of(t[0])) for t in TILES))
+    src.write_text(DRIVER % ", ".join("{%d, %d, %d, %d}" % (t[0], t[2], t[3], t[1]) for t in TILES))
     exe = d / "drv"
     subprocess.run([gxx, "-std=c++17", "-O1", f"-I{CSRC}", str(src), "-o", str(exe)], check=True)
     out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
     rows = {}
     for line in out.strip().splitlines():
         v = [int(x) for x in line.split()]
-        mt, ng, kg, xs, wd, kper = v[:6]
-        rows[(mt, ng, kg)] = dict(xs=xs, wd=wd, kper=kper, r0=v[6:10], rn=v[10:14],
-                                  w_issue=nr_of(mt) + 1)
+        mt, nr, ng, kg, xs, wd, kper = v[:7]
+        rows[(mt, nr, ng, kg)] = dict(xs=xs, wd=wd, kper=kper, r0=v[7:11], rn=v[11:15],
+                                      w_issue=nr + 1)
     assert set(rows) == set(TILES)
     return rows
 
@@ -107,8 +104,7 @@ def test_every_wait_covers_its_data(plans, tile):
 
 @pytest.mark.parametrize("tile", TILES)
 def test_ring_fits_lds(plans, tile):
-    mt, ng, kg = tile
-    nr = nr_of(mt)
+    mt, nr, ng, kg = tile
     p, wv = plans[tile], ng * kg
     ring = p["xs"] * kg * 16 * mt * 128 + p["wd"] * wv * (nr * 1024 + 256)
     red = (kg - 1) * ng * mt * nr * 256 * 4
