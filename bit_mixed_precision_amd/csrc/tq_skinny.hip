@@ -410,7 +410,11 @@ int skinny_stage(int64_t N, int64_t K, int64_t M) {
 int skinny_lwk(int64_t N, int64_t K, int64_t M) {
   const int RG = skinny_rows(N);
   const int64_t nb = K / 256;
-  const int64_t min_blocks = M <= 2 ? 8 : 1;
+  // At one or two activation rows, and at up to four with two or more row
+  // groups per workgroup, fewer waves that each take at least 8 blocks beat
+  // more waves (M = 4, N = K = 8192: 8 waves 8.6 us, 16 waves 9.4 us; with
+  // one row group 8 waves of 4 blocks still win: N = 3072, 6.3 against 7.1).
+  const int64_t min_blocks = (M <= 2 || (M <= 4 && RG >= 2)) ? 8 : 1;
   int lwk = 0;
   while ((RG << (lwk + 1)) <= 16 && (min_blocks << (lwk + 1)) <= nb) ++lwk;
   return lwk;
