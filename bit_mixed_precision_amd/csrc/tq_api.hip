@@ -87,7 +87,7 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
     case TQ_PATH_SKINNY:
       if (tq1)
         return Choice{tq::launch_tq1_skinny, "tq1_skinny_kernel", tq::tq1_depth(),
-                      tq::tq1_stage(N, K), tq::tq1_slices(M)};
+                      tq::tq1_stage(N, K, M), tq::tq1_slices(M)};
       if (M > kSkinnyMaxM) return Choice{nullptr, "", -1, -1};
       return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_depth(),
                     tq::skinny_stage(N, K, M)};

@@ -41,7 +41,7 @@ hipError_t launch_tq2_bwd_x(const void* dY, const void* qs, const void* scales, 
 // TQ1 MFMA kernel: any M, in slices of 16 activation rows.
 hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream);
 int tq1_depth();
-int tq1_stage(int64_t N, int64_t K);
+int tq1_stage(int64_t N, int64_t K, int64_t M);
 int tq1_slices(int64_t M);  // 16-row activation slices per workgroup (template argument)
 
 // Tiled MFMA kernels for M > 16: a workgroup of 4 waves (ng weight-row

@@ -406,21 +406,25 @@ int tq1_depth() { return kDepth1; }
 
 int tq1_slices(int64_t M) { return M <= 16 ? 1 : 2; }
 
-int tq1_lwk(int64_t N, int64_t K);
+int tq1_lwk(int64_t N, int64_t K, int64_t M);
 
-int tq1_stage(int64_t N, int64_t K) {
+int tq1_stage(int64_t N, int64_t K, int64_t M) {
   const int64_t RG = skinny_rows(N);
-  const int64_t threads = 64 * (RG << tq1_lwk(N, K));
+  const int64_t threads = 64 * (RG << tq1_lwk(N, K, M));
   return tq1_scale_bytes(RG, K) <= kScLds && 16 * RG * (K / 256) <= kScaleRegs * threads ? 1 : 0;
 }
 
 // Waves per row group: 2^lwk, at most 16 waves per workgroup and no more than
-// there are spans.
-int tq1_lwk(int64_t N, int64_t K) {
+// there are spans; from four activation rows on, with two or more row groups,
+// at most four per row group (N = K = 8192: M = 4 11.6 us with 8 waves
+// against 12.9 with 16, M = 16 20.3 against 22.3; at M = 1 16 waves stay
+// ahead, 9.5 against 9.7).
+int tq1_lwk(int64_t N, int64_t K, int64_t M) {
   const int RG = skinny_rows(N);
   const int64_t nu = ((K + 4) / 5 + 31) / 32;
+  const int max_lwk = M >= 4 && RG >= 2 ? 2 : 4;
   int lwk = 0;
-  while ((RG << (lwk + 1)) <= 16 && (int64_t{2} << lwk) <= nu) ++lwk;
+  while (lwk < max_lwk && (RG << (lwk + 1)) <= 16 && (int64_t{2} << lwk) <= nu) ++lwk;
   return lwk;
 }
 
@@ -456,7 +460,7 @@ hipError_t launch_tq1_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk)
 }
 
 hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream) {
-  return launch_tq1_skinny_lwk(a, stream, tq1_lwk(a.N, a.K));
+  return launch_tq1_skinny_lwk(a, stream, tq1_lwk(a.N, a.K, a.M));
 }
 
 }  // namespace tq
