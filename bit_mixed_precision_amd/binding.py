@@ -25,7 +25,10 @@ try:
 except ImportError:  # host-only use without torch: the system runtime is the only one
     _torch = None
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+# TQ_LIBRARY names another build of the same library (the sanitizer variant
+# of build_lib); by default the in-tree libtq.so next to this file.
+_LIB_PATH = os.environ.get("TQ_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 if not os.path.exists(_LIB_PATH):
     raise ImportError(f"{_LIB_PATH} is missing; build it with "
                       "`python -m bit_mixed_precision_amd.build_lib`")
@@ -184,68 +187,149 @@ def tq_unpack_tq1(qs: np.ndarray, K: int) -> np.ndarray:
 
 # ------------------------------------------------------------------ device
 
-def _stream(stream):
+_DTYPES = {"f16": "float16", "f32": "float32", "u8": "uint8", "i32": "int32"}
+
+
+def _need(t, name, dtype, shape=None, where=""):
+    """Check one device-tensor argument before its pointer reaches the C ABI,
+    which receives bare pointers and cannot check sizes itself: a buffer that
+    is too small would be read or written past its end.  Order: type and dtype
+    (TQ_ERR_VALUE), rank, shape and contiguity (TQ_ERR_SHAPE), then device
+    (TQ_ERR_DEVICE), so that every check but the last also runs without a GPU."""
+    import torch
+    if not torch.is_tensor(t):
+        raise TQError(TQ_ERR_VALUE, f"{where}: {name} must be a torch tensor")
+    if t.dtype != getattr(torch, _DTYPES[dtype]):
+        raise TQError(TQ_ERR_VALUE, f"{where}: {name} must be {_DTYPES[dtype]}, not {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise TQError(TQ_ERR_SHAPE, f"{where}: {name} has shape {tuple(t.shape)}, "
+                                    f"expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise TQError(TQ_ERR_SHAPE, f"{where}: {name} must be contiguous (row-major)")
+    return t
+
+
+def _on_gpu(where, *named):
+    """Every (name, tensor) on a GPU, all on the first one's device; run after
+    the dtype and shape checks of every argument."""
+    first = named[0][1]
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise TQError(TQ_ERR_DEVICE, f"{where}: {name} is on {t.device}, not on a GPU")
+        if t.device != first.device:
+            raise TQError(TQ_ERR_DEVICE, f"{where}: {name} is on {t.device}, "
+                                         f"{named[0][0]} on {first.device}")
+
+
+def _rank2(t, name, where):
+    import torch
+    if not torch.is_tensor(t) or t.dim() != 2:
+        raise TQError(TQ_ERR_SHAPE, f"{where}: {name} must be a 2-D tensor")
+    return t.shape
+
+
+def _stream(stream, device=None):
     if stream is not None:
         return stream
     import torch
-    return torch.cuda.current_stream().cuda_stream
+    return torch.cuda.current_stream(device).cuda_stream
 
 
-def _out(Y, M, N, like):
-    if Y is not None:
-        return Y
+def _out(Y, M, N, where, operands, name="Y"):
+    """The output: Y checked as fp16 [M][N] when given, then every operand's
+    device (``operands`` as (name, tensor) pairs); a new tensor on the first
+    operand's device when Y is None (allocated only after every check)."""
     import torch
-    return torch.empty((M, N), dtype=torch.float16, device=like.device)
+    if Y is not None:
+        _need(Y, name, "f16", (M, N), where)
+    _on_gpu(where, *operands, (name, Y))
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float16, device=operands[0][1].device)
+    return Y
+
+
+def _device_of(t):
+    """Context that makes t's GPU the current HIP device for the C call."""
+    import torch
+    return torch.cuda.device(t.device)
+
+
+def _gemm_operands(X, qs, scales, where, ldq_from_qs=False):
+    """(M, N, K, ldq) of a product after checking X [M][K] fp16, qs [N][K/4]
+    (TQ2) or [N][ldq] (TQ1) uint8 and scales [N][K/256] fp16."""
+    M, K = _rank2(X, "X", where)
+    N, qcols = _rank2(qs, "qs", where)
+    _need(X, "X", "f16", None, where)
+    _need(qs, "qs", "u8", (N, qcols if ldq_from_qs else K // 4), where)
+    if not ldq_from_qs and qcols * 4 != K:
+        raise TQError(TQ_ERR_SHAPE, f"{where}: qs has {qcols} bytes per row, expected K/4 = {K // 4}")
+    _need(scales, "scales", "f16", (N, K // 256), where)
+    return M, N, K, qcols
 
 
 def tq_gemm_tq2_ex(X, qs, scales, path: int, Y=None, stream=None):
     """Y[M][N] = X[M][K] (s . T)^T for TQ2 weights qs [N][K/4]; tensors on the GPU."""
-    M, K = X.shape
-    N = qs.shape[0]
-    Y = _out(Y, M, N, X)
-    _check(lib.tq_gemm_tq2_ex(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, path,
-                              _stream(stream)), "tq_gemm_tq2")
+    where = "tq_gemm_tq2"
+    M, N, K, _ = _gemm_operands(X, qs, scales, where)
+    Y = _out(Y, M, N, where, (("X", X), ("qs", qs), ("scales", scales)))
+    with _device_of(X):
+        _check(lib.tq_gemm_tq2_ex(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, path,
+                                  _stream(stream, X.device)), where)
     return Y
 
 
 def tq_gemm_tq1_ex(X, qs, scales, path: int, Y=None, stream=None):
     """Same as tq_gemm_tq2_ex for TQ1 weights qs [N][ldq] (ldq = qs.shape[1])."""
-    M, K = X.shape
-    N, ldq = qs.shape
-    Y = _out(Y, M, N, X)
-    _check(lib.tq_gemm_tq1_ex(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K, path,
-                              _stream(stream)), "tq_gemm_tq1")
+    where = "tq_gemm_tq1"
+    M, N, K, ldq = _gemm_operands(X, qs, scales, where, ldq_from_qs=True)
+    Y = _out(Y, M, N, where, (("X", X), ("qs", qs), ("scales", scales)))
+    with _device_of(X):
+        _check(lib.tq_gemm_tq1_ex(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K, path,
+                                  _stream(stream, X.device)), where)
     return Y
 
 
 def tq_gemm_tq2_tiled(X, qs, scales, mt: int, ng: int, kg: int, Y=None, stream=None):
     """tq_gemm_tq2 on the tiled kernel with an explicit (mt, ng, kg) tile."""
-    M, K = X.shape
-    N = qs.shape[0]
-    Y = _out(Y, M, N, X)
-    _check(lib.tq_gemm_tq2_tiled(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, ng, kg,
-                                 _stream(stream)), "tq_gemm_tq2_tiled")
+    where = "tq_gemm_tq2_tiled"
+    M, N, K, _ = _gemm_operands(X, qs, scales, where)
+    Y = _out(Y, M, N, where, (("X", X), ("qs", qs), ("scales", scales)))
+    with _device_of(X):
+        _check(lib.tq_gemm_tq2_tiled(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, ng,
+                                     kg, _stream(stream, X.device)), where)
     return Y
 
 
 def tq_gemm_tq2_swiglu(X, qs_gate, scales_gate, qs_up, scales_up, Y=None, stream=None):
     """silu(X G^T) * (X U^T) for TQ2 gate / up matrices, M <= 16, one launch."""
-    M, K = X.shape
-    N = qs_gate.shape[0]
-    Y = _out(Y, M, N, X)
-    _check(lib.tq_gemm_tq2_swiglu(_ptr(X), _ptr(qs_gate), _ptr(scales_gate), _ptr(qs_up),
-                                  _ptr(scales_up), _ptr(Y), M, N, K, _stream(stream)),
-           "tq_gemm_tq2_swiglu")
+    where = "tq_gemm_tq2_swiglu"
+    M, N, K, _ = _gemm_operands(X, qs_gate, scales_gate, where)
+    _need(qs_up, "qs_up", "u8", tuple(qs_gate.shape), where)
+    _need(scales_up, "scales_up", "f16", tuple(scales_gate.shape), where)
+    Y = _out(Y, M, N, where, (("X", X), ("qs_gate", qs_gate), ("scales_gate", scales_gate),
+                              ("qs_up", qs_up), ("scales_up", scales_up)))
+    with _device_of(X):
+        _check(lib.tq_gemm_tq2_swiglu(_ptr(X), _ptr(qs_gate), _ptr(scales_gate), _ptr(qs_up),
+                                      _ptr(scales_up), _ptr(Y), M, N, K,
+                                      _stream(stream, X.device)), where)
     return Y
 
 
 def tq_gemm_tq2_bwd_x(dY, qs, scales, dX=None, stream=None):
     """dX = dY (s . T): the input gradient of tq_gemm_tq2 (N % 8 == 0)."""
-    M, N = dY.shape
-    K = qs.shape[1] * 4
-    dX = _out(dX, M, K, dY)
-    _check(lib.tq_gemm_tq2_bwd_x(_ptr(dY), _ptr(qs), _ptr(scales), _ptr(dX), M, N, K,
-                                 _stream(stream)), "tq_gemm_tq2_bwd_x")
+    where = "tq_gemm_tq2_bwd_x"
+    M, N = _rank2(dY, "dY", where)
+    _, qcols = _rank2(qs, "qs", where)
+    K = qcols * 4
+    _need(dY, "dY", "f16", None, where)
+    _need(qs, "qs", "u8", (N, qcols), where)
+    _need(scales, "scales", "f16", (N, K // 256), where)
+    dX = _out(dX, M, K, where, (("dY", dY), ("qs", qs), ("scales", scales)), name="dX")
+    with _device_of(dY):
+        _check(lib.tq_gemm_tq2_bwd_x(_ptr(dY), _ptr(qs), _ptr(scales), _ptr(dX), M, N, K,
+                                     _stream(stream, dY.device)), where)
     return dX
 
 
@@ -259,11 +343,17 @@ def tq_tq1_transcode_min_m(N: int, K: int) -> int:
 def tq_transcode_tq1_tq2(qs1, K: int, qs2=None, stream=None):
     """TQ2 bytes [N][K/4] (uint8, device) holding the trits of the TQ1 rows qs1 [N][ldq]."""
     import torch
-    N, ldq = qs1.shape
+    where = "tq_transcode_tq1_tq2"
+    N, ldq = _rank2(qs1, "qs1", where)
+    _need(qs1, "qs1", "u8", None, where)
+    if qs2 is not None:
+        _need(qs2, "qs2", "u8", (N, K // 4), where)
+    _on_gpu(where, ("qs1", qs1), ("qs2", qs2))
     if qs2 is None:
         qs2 = torch.empty((N, K // 4), dtype=torch.uint8, device=qs1.device)
-    _check(lib.tq_transcode_tq1_tq2(_ptr(qs1), ldq, N, K, _ptr(qs2), _stream(stream)),
-           "tq_transcode_tq1_tq2")
+    with _device_of(qs1):
+        _check(lib.tq_transcode_tq1_tq2(_ptr(qs1), ldq, N, K, _ptr(qs2),
+                                        _stream(stream, qs1.device)), where)
     return qs2
 
 
@@ -271,39 +361,57 @@ def tq_gemm_tq1_ws(X, qs, scales, workspace, Y=None, stream=None):
     """tq_gemm_tq1 with a workspace (uint8 device tensor of at least N * K / 4
     bytes): from tq_tq1_transcode_min_m(N, K) rows on, the weights are
     transcoded once into it and the TQ2 kernels run."""
-    M, K = X.shape
-    N, ldq = qs.shape
-    Y = _out(Y, M, N, X)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.tq_gemm_tq1_ws(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K,
-                              _ptr(workspace), nbytes, _stream(stream)), "tq_gemm_tq1_ws")
+    where = "tq_gemm_tq1_ws"
+    M, N, K, ldq = _gemm_operands(X, qs, scales, where, ldq_from_qs=True)
+    nbytes = 0
+    if workspace is not None:
+        _need(workspace, "workspace", "u8", None, where)
+        nbytes = workspace.numel()
+    Y = _out(Y, M, N, where, (("X", X), ("qs", qs), ("scales", scales), ("workspace", workspace)))
+    with _device_of(X):
+        _check(lib.tq_gemm_tq1_ws(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K,
+                                  _ptr(workspace), nbytes, _stream(stream, X.device)), where)
     return Y
 
 
 def tq_stream_read(src, sink, stream=None):
     """Read every byte of the contiguous device tensor src once (the practical
-    read ceiling); sink is a device tensor of at least 4 bytes."""
+    read ceiling); sink is an int32 device tensor of at least one element."""
+    where = "tq_stream_read"
+    import torch
+    if not torch.is_tensor(src):
+        raise TQError(TQ_ERR_VALUE, f"{where}: src must be a torch tensor")
+    if not src.is_contiguous():
+        raise TQError(TQ_ERR_SHAPE, f"{where}: src must be contiguous")
+    _need(sink, "sink", "i32", None, where)
+    if sink.numel() < 1:
+        raise TQError(TQ_ERR_SHAPE, f"{where}: sink needs at least one int32")
+    _on_gpu(where, ("src", src), ("sink", sink))
     nbytes = src.numel() * src.element_size()
-    _check(lib.tq_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "tq_stream_read")
+    with _device_of(src):
+        _check(lib.tq_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream, src.device)),
+               where)
 
 
 def tq_gemm_tq2_tile(X, qs, scales, mt: int, nr: int, ng: int, kg: int, Y=None, stream=None):
     """tq_gemm_tq2 on the tiled kernel with an explicit (mt, nr, ng, kg) tile."""
-    M, K = X.shape
-    N = qs.shape[0]
-    Y = _out(Y, M, N, X)
-    _check(lib.tq_gemm_tq2_tile(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, nr, ng, kg,
-                                _stream(stream)), "tq_gemm_tq2_tile")
+    where = "tq_gemm_tq2_tile"
+    M, N, K, _ = _gemm_operands(X, qs, scales, where)
+    Y = _out(Y, M, N, where, (("X", X), ("qs", qs), ("scales", scales)))
+    with _device_of(X):
+        _check(lib.tq_gemm_tq2_tile(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, nr, ng,
+                                    kg, _stream(stream, X.device)), where)
     return Y
 
 
 def tq_gemm_tq1_tiled(X, qs, scales, mt: int, nw: int, kg: int, Y=None, stream=None):
     """tq_gemm_tq1 on the tiled kernel with an explicit (mt, nw, kg) tile."""
-    M, K = X.shape
-    N, ldq = qs.shape
-    Y = _out(Y, M, N, X)
-    _check(lib.tq_gemm_tq1_tiled(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K, mt, nw,
-                                 kg, _stream(stream)), "tq_gemm_tq1_tiled")
+    where = "tq_gemm_tq1_tiled"
+    M, N, K, ldq = _gemm_operands(X, qs, scales, where, ldq_from_qs=True)
+    Y = _out(Y, M, N, where, (("X", X), ("qs", qs), ("scales", scales)))
+    with _device_of(X):
+        _check(lib.tq_gemm_tq1_tiled(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K, mt,
+                                     nw, kg, _stream(stream, X.device)), where)
     return Y
 
 
@@ -311,7 +419,12 @@ def tq_pack_dev(fmt: int, W, eps: float = 1e-5, ldq: int | None = None, stream=N
     """On-device ternarize + pack of a float32 [N][K] device tensor W (fmt 2 or 1).
     Returns device tensors (qs, scales fp16, gamma fp64 [1], status int32 [1])."""
     import torch
-    N, K = W.shape
+    where = "tq_pack_tq%d_dev" % fmt
+    if fmt not in (1, 2):
+        raise TQError(TQ_ERR_VALUE, f"{where}: format must be 1 or 2")
+    N, K = _rank2(W, "W", where)
+    _need(W, "W", "f32", None, where)
+    _on_gpu(where, ("W", W))
     dev = W.device
     if fmt == 2:
         qs = torch.empty((N, K // 4), dtype=torch.uint8, device=dev)
@@ -325,13 +438,15 @@ def tq_pack_dev(fmt: int, W, eps: float = 1e-5, ldq: int | None = None, stream=N
     if wsb < 0:
         raise TQError(TQ_ERR_SHAPE, "tq_pack_dev_workspace_bytes")
     ws = torch.empty(int(wsb), dtype=torch.uint8, device=dev)
-    if fmt == 2:
-        st = lib.tq_pack_tq2_dev(_ptr(W), N, K, float(eps), _ptr(qs), _ptr(scales), _ptr(gamma),
-                                 _ptr(status), _ptr(ws), wsb, _stream(stream))
-    else:
-        st = lib.tq_pack_tq1_dev(_ptr(W), N, K, float(eps), ldq, _ptr(qs), _ptr(scales),
-                                 _ptr(gamma), _ptr(status), _ptr(ws), wsb, _stream(stream))
-    _check(st, "tq_pack_tq%d_dev" % fmt)
+    with _device_of(W):
+        sp = _stream(stream, dev)
+        if fmt == 2:
+            st = lib.tq_pack_tq2_dev(_ptr(W), N, K, float(eps), _ptr(qs), _ptr(scales),
+                                     _ptr(gamma), _ptr(status), _ptr(ws), wsb, sp)
+        else:
+            st = lib.tq_pack_tq1_dev(_ptr(W), N, K, float(eps), ldq, _ptr(qs), _ptr(scales),
+                                     _ptr(gamma), _ptr(status), _ptr(ws), wsb, sp)
+    _check(st, where)
     return qs, scales, gamma, status
 
 

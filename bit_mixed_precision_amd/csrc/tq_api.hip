@@ -14,6 +14,9 @@ namespace {
 constexpr int64_t kMaxMN = int64_t(1) << 24;
 constexpr int64_t kMaxK = int64_t(1) << 20;
 constexpr int64_t kMaxBwdN = int64_t(1) << 20;  // 32-bit offsets in 512 rows of dY
+// Largest TQ1 row stride: the kernels take it as a 32-bit int and form byte
+// offsets such as 16 rows * ldq inside a workgroup in 32 bits.
+constexpr int64_t kMaxLdq = int64_t(1) << 24;
 // Activation rows from which a TQ1 product with a workspace transcodes the
 // weights once and runs the TQ2 kernels.  The TQ1 kernels cost a step per 16
 // (skinny) or 32 rows (two slices); the transcoding a fixed read and write of
@@ -36,7 +39,7 @@ int check_gemm(const void* X, const void* qs, const void* scales, const void* Y,
   }
   if (!X || !qs || !scales || !Y) return TQ_ERR_NULL;
   if (M > kMaxMN || N > kMaxMN || K < 256 || K % 256 || K > kMaxK) return TQ_ERR_SHAPE;
-  if (tq1 && (ldq < (K + 4) / 5 || ldq % 16)) return TQ_ERR_SHAPE;
+  if (tq1 && (ldq < (K + 4) / 5 || ldq % 16 || ldq > kMaxLdq)) return TQ_ERR_SHAPE;
   if (!aligned16(X) || !aligned16(qs) || !aligned16(scales) || !aligned16(Y)) return TQ_ERR_ALIGN;
   return TQ_OK;
 }
@@ -134,6 +137,17 @@ int device_cus() {
   }
   cache[dev].store(cus, std::memory_order_relaxed);
   return cus;
+}
+
+hipError_t lds_limit_once(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? uint64_t{1} << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
 }
 
 }  // namespace tq
@@ -290,7 +304,8 @@ int tq_transcode_tq1_tq2(const void* qs1, int64_t ldq, int64_t N, int64_t K, voi
   if (N < 0) return TQ_ERR_SHAPE;
   if (N == 0) return TQ_OK;
   if (!qs1 || !qs2) return TQ_ERR_NULL;
-  if (N > kMaxMN || K < 256 || K % 256 || K > kMaxK || ldq < (K + 4) / 5 || ldq % 16)
+  if (N > kMaxMN || K < 256 || K % 256 || K > kMaxK || ldq < (K + 4) / 5 || ldq % 16 ||
+      ldq > kMaxLdq)
     return TQ_ERR_SHAPE;
   if (!aligned16(qs1) || !aligned16(qs2)) return TQ_ERR_ALIGN;
   int st = device_ready();

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace tq {
 
 struct GemmArgs {
@@ -19,6 +21,13 @@ struct GemmArgs {
 
 // Number of compute units of the current device (cached per device).
 int device_cus();
+
+// Raises the dynamic-LDS limit of kernel `fn` to `bytes` on the current device
+// the first time a launcher needs it there.  `done` holds one bit per device
+// (devices 0..63) and is shared by every call for that kernel, so concurrent
+// first calls from several host threads are safe: each sets the attribute (an
+// idempotent call) before it launches, and no device inherits another's bit.
+hipError_t lds_limit_once(const void* fn, int bytes, std::atomic<uint64_t>& done);
 
 hipError_t launch_tq2_simple(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_tq1_simple(const GemmArgs& a, hipStream_t stream);

@@ -364,14 +364,10 @@ constexpr int kDepth = 4;
 template <bool STAGE, bool GLU>
 hipError_t launch_tq2_skinny_s(const GemmArgs& a, const void* qs2, const void* scales2,
                                hipStream_t stream, int RG, int lwk, int nbw, int xregion, int lds) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(tq2_skinny_kernel<kDepth, STAGE, GLU>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = lds_limit_once(
+      reinterpret_cast<const void*>(tq2_skinny_kernel<kDepth, STAGE, GLU>), kLdsLimit, lds_set);
+  if (e != hipSuccess) return e;
   const int RGO = GLU ? RG / 2 : RG;
   const int64_t groups = (a.N + 16 * RGO - 1) / (16 * RGO);
   hipLaunchKernelGGL((tq2_skinny_kernel<kDepth, STAGE, GLU>), dim3((unsigned)groups),

@@ -423,14 +423,10 @@ constexpr int64_t kMOuterTiles = 4;
 template <int MT, int NR, int NG, int KG>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
   using G = TileGeom<MT, NR, NG, KG>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(tq2_tiled_kernel<MT, NR, NG, KG>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = lds_limit_once(reinterpret_cast<const void*>(tq2_tiled_kernel<MT, NR, NG, KG>),
+                                G::kLds, lds_set);
+  if (e != hipSuccess) return e;
   const int64_t n_tiles = (a.N + G::BN - 1) / G::BN;
   const int64_t m_tiles = (a.M + G::BM - 1) / G::BM;
   const int64_t groups = (n_tiles + 7) / 8;

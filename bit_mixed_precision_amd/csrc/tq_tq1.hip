@@ -374,14 +374,10 @@ constexpr int kDepth1 = 3;
 template <bool STAGE, int MS>
 hipError_t launch_tq1_s(const GemmArgs& a, hipStream_t stream, dim3 grid, int W, int lds, int RG,
                         int lwk, int nuw, int xregion) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(tq1_skinny_kernel<kDepth1, STAGE, MS>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = lds_limit_once(
+      reinterpret_cast<const void*>(tq1_skinny_kernel<kDepth1, STAGE, MS>), kLdsMax, lds_set);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((tq1_skinny_kernel<kDepth1, STAGE, MS>), grid, dim3(64 * W), lds, stream,
                      static_cast<const uint16_t*>(a.X), static_cast<const uint8_t*>(a.qs),
                      (int)a.ldq, static_cast<const uint16_t*>(a.scales),

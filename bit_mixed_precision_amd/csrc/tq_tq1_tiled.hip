@@ -328,14 +328,10 @@ hipError_t launch_t1(const GemmArgs& a, hipStream_t stream) {
   using G = T1Geom<MT, NW, KG>;
   constexpr int D = kDepthT1;
   constexpr int XP = xahead(NW, KG);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(tq1_tiled_kernel<MT, NW, KG, D, XP>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, G::kLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = lds_limit_once(
+      reinterpret_cast<const void*>(tq1_tiled_kernel<MT, NW, KG, D, XP>), G::kLds, lds_set);
+  if (e != hipSuccess) return e;
   const int64_t n_tiles = (a.N + G::BN - 1) / G::BN;
   const int64_t m_tiles = (a.M + G::BM - 1) / G::BM;
   // grid: n tiles rounded up to whole groups of 8 (one per XCD)

@@ -126,8 +126,9 @@ int tq_unpack_tq1(const uint8_t* qs, int64_t N, int64_t K, int64_t ldq, int8_t* 
  *   Y = X (s . T)^T :  X fp16 [M][K], Y fp16 [M][N], scales fp16 [N][K/256].
  *
  * Shapes: M, N >= 0 (M == 0 or N == 0 is a no-op that touches no pointer);
- * K a positive multiple of 256; M, N <= 2^24, K <= 2^20.  For TQ1, ldq >=
- * ceil(K/5) and ldq % 16 == 0.  X, qs, scales and Y must be 16-byte aligned.
+ * K a positive multiple of 256; M, N <= 2^24, K <= 2^20.  For TQ1,
+ * ceil(K/5) <= ldq <= 2^24 and ldq % 16 == 0.  X, qs, scales and Y must be
+ * 16-byte aligned.
  * Accumulation is fp32; Y is rounded to fp16 (nearest even) once, overflow
  * gives +-inf.  Trits are not validated on the device: a TQ2 field equal to 3
  * or an unused TQ1 byte gives unspecified (finite) values for that row.
@@ -229,8 +230,8 @@ int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales_f16, vo
  * ([N][K/4], "2 bits per weight"), bit for bit what tq_pack_tq2 writes for
  * the same trits; the block scales are shared unchanged.  Device pointers,
  * 16-byte aligned, owned by the caller; qs2 holds tq_tq2_bytes(N, K) bytes.
- * K a multiple of 256, ldq >= ceil(K/5) and a multiple of 16 (TQ_ERR_SHAPE
- * otherwise); N = 0 is a no-op.  Byte values that no trit group encodes are
+ * K a multiple of 256, ceil(K/5) <= ldq <= 2^24 and ldq a multiple of 16
+ * (TQ_ERR_SHAPE otherwise); N = 0 is a no-op.  Byte values that no trit group encodes are
  * not detected. */
 int tq_transcode_tq1_tq2(const void* qs1, int64_t ldq, int64_t N, int64_t K, void* qs2,
                          void* stream);

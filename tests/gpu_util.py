@@ -4,7 +4,7 @@ import functools
 
 import numpy as np
 
-from oracle import gemm_ref
+from oracle import dequantize_ref, gemm_ref
 from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
 
 #: Acceptance bound of the product: max|Y - Y_ref| <= REL_TOL * max|Y_ref|.
@@ -44,3 +44,29 @@ def activations(M, K, seed):
 
 def ref(X, T, s, cols=None):
     return gemm_ref(X, T, s, cols=cols)
+
+
+class DenseRef:
+    """The oracle's product for one (T, s) and several X: ``dequantize_ref``
+    once, then ``X64 @ Wd.T`` per call, the same arithmetic as ``gemm_ref``
+    without rebuilding the fp64 matrix (1.9 GB at 28672 x 8192) every time."""
+
+    def __init__(self, T, s):
+        self.WdT = dequantize_ref(T, s).T
+
+    def __call__(self, X, cols=None):
+        W = self.WdT if cols is None else self.WdT[:, np.asarray(cols)]
+        return np.asarray(X).astype(np.float64) @ W
+
+
+def strat_cols(N, seed, group=16, edge=32):
+    """Columns for a sampled check of a wide output: one random column in every
+    ``group`` consecutive columns, plus the first and last column of every
+    ``edge``-column tile (so both edges of every 32-, 64- and 128-wide weight
+    tile and every row group of 16), sorted and unique."""
+    rng = np.random.default_rng(seed)
+    starts = np.arange(0, N, group)
+    pick = starts + rng.integers(0, group, size=starts.size)
+    tiles = np.arange(0, N, edge)
+    cols = np.concatenate([pick, tiles, np.minimum(tiles + edge - 1, N - 1), [N - 1]])
+    return np.unique(cols[cols < N])

@@ -167,7 +167,9 @@ def test_package_fails_loudly_without_library(tmp_path):
                     ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
     code = ("import bit_mixed_precision_amd as b\n"
             "try:\n    b.tq_gemm_tq2\nexcept ImportError as e:\n    print('IMPORT-ERROR', e)\n")
-    out = subprocess.run(["python", "-c", code], cwd=tmp_path, capture_output=True, text=True)
+    env = {k: v for k, v in os.environ.items() if k != "TQ_LIBRARY"}  # the default path only
+    out = subprocess.run(["python", "-c", code], cwd=tmp_path, capture_output=True, text=True,
+                         env=env)
     assert "IMPORT-ERROR" in out.stdout, out.stdout + out.stderr
 
 
@@ -263,3 +265,75 @@ def test_gemm_tq1_ws_argument_errors():
     assert call(X=None) == tq.TQ_ERR_NULL
     assert call(nb=-1) == tq.TQ_ERR_SHAPE
     assert call(ws=A + 4) == tq.TQ_ERR_ALIGN
+
+
+def test_ldq_upper_bound():
+    """The TQ1 kernels take ldq as a 32-bit int: strides past 2^24 are refused
+    before any device work (else row offsets could wrap)."""
+    big = (1 << 24) + 16
+    assert _g1(ldq=big) == tq.TQ_ERR_SHAPE
+    assert _g1(ldq=1 << 31) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_gemm_tq1_tiled", A, A, big, A, A, 40, 64, 512, 2, 4, 4,
+                       None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_transcode_tq1_tq2", A, big, 4, 8192, A, None) == tq.TQ_ERR_SHAPE
+    assert tq.raw_call("tq_gemm_tq1_ws", A, A, big, A, A, 64, 16, 256, A, 1 << 20,
+                       None) == tq.TQ_ERR_SHAPE
+
+
+# ---- the Python binding's checks of its tensor arguments (no device needed:
+# every check but the last, the device, runs on CPU tensors)
+
+def _t(shape, dtype):
+    torch = pytest.importorskip("torch")
+    return torch.zeros(shape, dtype=getattr(torch, dtype))
+
+
+def _raises(status, fn, *a, **kw):
+    with pytest.raises(tq.TQError) as e:
+        fn(*a, **kw)
+    assert e.value.status == status, str(e.value)
+
+
+def test_binding_rejects_bad_gemm_tensors():
+    X, q, s = _t((4, 512), "float16"), _t((32, 128), "uint8"), _t((32, 2), "float16")
+    # well-formed CPU tensors get as far as the device check
+    _raises(tq.TQ_ERR_DEVICE, tq.tq_gemm_tq2, X, q, s)
+    _raises(tq.TQ_ERR_VALUE, tq.tq_gemm_tq2, X.float(), q, s)
+    _raises(tq.TQ_ERR_VALUE, tq.tq_gemm_tq2, X, q.int(), s)
+    _raises(tq.TQ_ERR_VALUE, tq.tq_gemm_tq2, X, q, s.float())
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2, X, _t((32, 64), "uint8"), s)    # qs too short
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2, X, q, _t((32, 1), "float16"))  # scales too short
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2, X, q, _t((31, 2), "float16"))
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2, X.t(), q, s)                   # transposed X
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2, _t((512, 4), "float16").t(), q, s)  # not contiguous
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2, X[0], q, s)                    # not 2-D
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2, X, q, s, _t((4, 31), "float16"))   # short Y
+    _raises(tq.TQ_ERR_VALUE, tq.tq_gemm_tq2, X, q, s, _t((4, 32), "float32"))   # wrong Y dtype
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2_tile, X, q, _t((32, 1), "float16"), 2, 2, 1, 4)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2_tiled, X, _t((16, 128), "uint8"), s, 2, 1, 4)
+    # TQ1: qs [N][ldq]; scales still [N][K/256]
+    q1 = _t((32, 112), "uint8")
+    _raises(tq.TQ_ERR_DEVICE, tq.tq_gemm_tq1, X, q1, s)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq1, X, q1, _t((32, 4), "float16"))
+    _raises(tq.TQ_ERR_VALUE, tq.tq_gemm_tq1, X, q1.half(), s)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq1_tiled, X, q1, _t((16, 2), "float16"), 2, 4, 4)
+    _raises(tq.TQ_ERR_DEVICE, tq.tq_gemm_tq1_ws, X, q1, s, _t((32 * 128,), "uint8"))
+    _raises(tq.TQ_ERR_VALUE, tq.tq_gemm_tq1_ws, X, q1, s, _t((32 * 128,), "int32"))
+
+
+def test_binding_rejects_bad_other_tensors():
+    X, q, s = _t((4, 512), "float16"), _t((32, 128), "uint8"), _t((32, 2), "float16")
+    _raises(tq.TQ_ERR_DEVICE, tq.tq_gemm_tq2_swiglu, X, q, s, q, s)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2_swiglu, X, q, s, _t((16, 128), "uint8"), s)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2_swiglu, X, q, s, q, _t((32, 1), "float16"))
+    dY = _t((4, 32), "float16")
+    _raises(tq.TQ_ERR_DEVICE, tq.tq_gemm_tq2_bwd_x, dY, q, s)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2_bwd_x, _t((4, 16), "float16"), q, s)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq2_bwd_x, dY, q, s, _t((4, 256), "float16"))
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_transcode_tq1_tq2, _t((32, 112), "uint8"), 512,
+            _t((32, 64), "uint8"))
+    _raises(tq.TQ_ERR_DEVICE, tq.tq_transcode_tq1_tq2, _t((32, 112), "uint8"), 512)
+    _raises(tq.TQ_ERR_VALUE, tq.tq_pack_dev, 2, _t((32, 512), "float16"))
+    _raises(tq.TQ_ERR_DEVICE, tq.tq_pack_dev, 2, _t((32, 512), "float32"))
+    _raises(tq.TQ_ERR_VALUE, tq.tq_stream_read, _t((64,), "uint8"), _t((4,), "float32"))
+    _raises(tq.TQ_ERR_DEVICE, tq.tq_stream_read, _t((64,), "uint8"), _t((4,), "int32"))
