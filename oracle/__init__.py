@@ -23,4 +23,5 @@ from .tq_oracle import (  # noqa: F401
     silu_ref,
     swiglu_ref,
     gemm_bwd_x_ref,
+    ste_grad_w_ref,
 )

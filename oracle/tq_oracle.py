@@ -299,3 +299,36 @@ def gemm_bwd_x_ref(dY, T, scales, cols=None) -> np.ndarray:
     if dY64.shape[1] != Wd.shape[0]:
         raise ValueError("dY and T disagree on N")
     return dY64 @ Wd
+
+
+def ste_grad_w_ref(dY, X, dW_in=None, rows=None) -> np.ndarray:
+    """Gradient that reaches the latent weights of one ternary linear, in fp64.
+
+    "The model" (project page) and "Architecture of TriLM and FloatLM" (Spectra
+    page): the forward pass uses the effective weights gamma * T, with
+    T = round(clip(W / gamma, -1, 1)), and a straight-through estimator carries
+    the gradient back to the latent floating-point weights W.  Read plainly,
+    the estimator treats the whole quantizer W -> gamma * T as the identity in
+    the backward pass, so the latent weights receive exactly the gradient of
+    the loss with respect to the effective weights of Y = X (gamma T)^T:
+
+        dW[n][k] = sum_m dY[m][n] * X[m][k]      (dW = dY^T X)
+
+    with gamma not differentiated and no mask outside the clip window (the
+    pages name none).  It does not depend on W, gamma or T.  ``dW_in`` (fp32
+    or fp64 [N][K]) is added when given: gradient accumulation over
+    micro-batches.  ``rows`` restricts the output rows n.
+    """
+    dY64 = np.asarray(dY).astype(np.float64)
+    X64 = np.asarray(X).astype(np.float64)
+    if dY64.ndim != 2 or X64.ndim != 2 or dY64.shape[0] != X64.shape[0]:
+        raise ValueError("dY [M][N] and X [M][K] must share M")
+    if rows is not None:
+        dY64 = dY64[:, np.asarray(rows)]
+    G = dY64.T @ X64
+    if dW_in is not None:
+        base = np.asarray(dW_in).astype(np.float64)
+        if rows is not None:
+            base = base[np.asarray(rows)]
+        G = base + G
+    return G

@@ -403,3 +403,71 @@ def test_bwd_x_column_sampling():
     cols = np.array([0, 255, 256, 511, 700, K - 1])
     full = gemm_bwd_x_ref(dY, T, s)
     np.testing.assert_array_equal(gemm_bwd_x_ref(dY, T, s, cols=cols), full[:, cols])
+
+
+# ---- gradient to the latent weights (straight-through estimator)
+
+def test_ste_grad_w_adjoint_and_brute_force():
+    """<X (s.T)^T, dY> = <s.T, dW> for any (T, s): the weight gradient is the
+    adjoint of gemm_ref in its weight argument (a transposed operand or a
+    dropped row fails it); math.fsum brute force on a tiny case; accumulation
+    adds exactly."""
+    from oracle import ste_grad_w_ref
+    rng = np.random.default_rng(24)
+    M, N, K = 6, 9, 512
+    T = rng.integers(-1, 2, (N, K)).astype(np.int8)
+    s = rng.uniform(0.01, 0.1, (N, K // 256)).astype(np.float16)
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    dY = rng.standard_normal((M, N)).astype(np.float16)
+    G = ste_grad_w_ref(dY, X)
+    assert G.shape == (N, K)
+    lhs = math.fsum((gemm_ref(X, T, s) * dY.astype(np.float64)).ravel())
+    rhs = math.fsum((dequantize_ref(T, s) * G).ravel())
+    assert abs(lhs - rhs) <= 1e-11 * max(1.0, abs(lhs))
+    for n in (0, 4, N - 1):
+        for k in (0, 255, 256, K - 1):
+            want = math.fsum(float(dY[m, n]) * float(X[m, k]) for m in range(M))
+            assert abs(G[n, k] - want) <= 1e-12 * max(1.0, abs(want))
+    base = rng.standard_normal((N, K)).astype(np.float32)
+    np.testing.assert_array_equal(ste_grad_w_ref(dY, X, base), base.astype(np.float64) + G)
+    rows = np.array([0, 3, N - 1])
+    np.testing.assert_array_equal(ste_grad_w_ref(dY, X, base, rows=rows), (base + G)[rows])
+
+
+def test_ste_grad_w_special_cases():
+    """One activation row: dW is the outer product dY[0]^T X[0], exactly (a
+    product of two fp16 values is exact in fp64).  X the identity (M = K):
+    dW = dY^T.  Zero upstream gradient: dW = 0."""
+    from oracle import ste_grad_w_ref
+    rng = np.random.default_rng(25)
+    dY = rng.standard_normal((1, 40)).astype(np.float16)
+    X = rng.standard_normal((1, 256)).astype(np.float16)
+    np.testing.assert_array_equal(ste_grad_w_ref(dY, X),
+                                  np.outer(dY[0].astype(np.float64), X[0].astype(np.float64)))
+    d = rng.standard_normal((256, 24)).astype(np.float16)
+    np.testing.assert_array_equal(ste_grad_w_ref(d, np.eye(256, dtype=np.float16)),
+                                  d.T.astype(np.float64))
+    assert not ste_grad_w_ref(np.zeros((5, 8), np.float16), X.repeat(5, 0)).any()
+
+
+def test_ste_grad_w_matches_autograd_of_the_model():
+    """The layer of "The model" written in torch (fp64, CPU) with the common
+    straight-through idiom W + (gamma T - W).detach(): autograd's gradient
+    of <Y, dY> with respect to the latent W is ste_grad_w_ref, whatever the
+    latents (so gamma is not differentiated and nothing is masked, also for
+    |W / gamma| > 1)."""
+    torch = pytest.importorskip("torch")
+    from oracle import ste_grad_w_ref
+    rng = np.random.default_rng(26)
+    M, N, K = 7, 12, 256
+    W0 = latent_weights_f32(rng, N, K, 0.02)
+    W0[0, :8] = 0.5  # far outside the clip window
+    X = rng.standard_normal((M, K)).astype(np.float16)
+    dY = rng.standard_normal((M, N)).astype(np.float16)
+    W = torch.tensor(W0.astype(np.float64), requires_grad=True)
+    T, g = ternarize_ref(W0, 1e-5)
+    q = torch.tensor(g * T.astype(np.float64))
+    w_eff = W + (q - W).detach()
+    Y = torch.tensor(X.astype(np.float64)) @ w_eff.T
+    (Y * torch.tensor(dY.astype(np.float64))).sum().backward()
+    np.testing.assert_allclose(W.grad.numpy(), ste_grad_w_ref(dY, X), rtol=0, atol=1e-12)
