@@ -41,7 +41,10 @@ def tq1_ldq(K):
 
 def alg_bytes(fmt, M, N, K):
     """Bytes the method must move: packed weights, scales, X, Y (for "bwd":
-    dY [M][N] in, dX [M][K] out, the same sizes)."""
+    dY [M][N] in, dX [M][K] out, the same sizes; for "ste", the latent-weight
+    gradient: dY [M][N] and X [M][K] in, dW [N][K] fp32 out)."""
+    if fmt == "ste":
+        return 2 * M * N + 2 * M * K + 4 * N * K
     w = N * K // 4 if fmt in ("tq2", "bwd") else N * tq1_ldq(K)
     return w + 2 * N * (K // 256) + 2 * M * K + 2 * M * N
 
@@ -71,6 +74,8 @@ PREFILL_MS = [256, 1024, 4096]
 # ((N, K) = (8192, 8192) for q / o, (28672, 8192) for gate / up, (8192,
 # 28672) for down) at 4096 tokens.
 BWD_CALLS = [("bwd", 4096, 8192, 8192), ("bwd", 4096, 28672, 8192), ("bwd", 4096, 8192, 28672)]
+# ... and the gradient reaching the latent weights, dW = dY^T X (fp32), same shapes
+BWD_CALLS += [("ste", M, N, K) for _, M, N, K in BWD_CALLS]
 
 
 def prefill_calls():
@@ -89,7 +94,7 @@ def build_inputs(torch, tq, calls):
     rings = {}
     for fmt, M, N, K in calls:
         key = (fmt, N, K)
-        if key in rings:
+        if key in rings or fmt == "ste":  # dense operands only: nothing packed
             continue
         rng = seed_for(500, N, K, 1 if fmt == "tq2" else 2)
         T = ternary_iid(rng, N, K, 0.31 if fmt == "tq2" else 0.3)
@@ -105,6 +110,14 @@ def build_inputs(torch, tq, calls):
         log(f"[bench] {fmt} N={N} K={K}: {R} buffer sets of {per_set / 1e6:.1f} MB")
     xs, ys = {}, {}
     for fmt, M, N, K in calls:
+        if fmt == "ste":
+            for shape in ((M, N), (M, K)):
+                if shape not in xs:
+                    xs[shape] = torch.from_numpy(activations_fp16(seed_for(501, *shape),
+                                                                  *shape)).cuda()
+            if ("w", N, K) not in ys:
+                ys[("w", N, K)] = torch.empty((N, K), dtype=torch.float32, device="cuda")
+            continue
         xin, yout = ((M, N), (M, K)) if fmt == "bwd" else ((M, K), (M, N))
         if xin not in xs:
             xs[xin] = torch.from_numpy(activations_fp16(seed_for(501, *xin), *xin)).cuda()
@@ -116,6 +129,12 @@ def build_inputs(torch, tq, calls):
 
 
 def run_call(tq, fmt, M, N, K, rings, xs, ys, stream):
+    if fmt == "ste":
+        dY, X, dW = xs[(M, N)], xs[(M, K)], ys[("w", N, K)]
+        st = tq.lib.tq_ste_grad_w(dY.data_ptr(), X.data_ptr(), dW.data_ptr(), M, N, K, 0, stream)
+        if st != 0:
+            raise RuntimeError(f"tq_ste_grad_w failed: {tq.tq_status_string(st)}")
+        return
     r = rings[(fmt, N, K)]
     q, s = r["sets"][r["next"]]
     r["next"] = (r["next"] + 1) % len(r["sets"])
@@ -147,6 +166,8 @@ def kernel_label(tq, fmt, M, N, K):
     """The kernel(s) a call runs, as profilers name them."""
     if fmt == "bwd":
         return "tq2_bwd_x_kernel"
+    if fmt == "ste":
+        return "tq_ste_grad_w_kernel"
     if fmt == "tq1" and M >= tq.tq_tq1_transcode_min_m(N, K):
         return "tq1_to_tq2_kernel + " + tq.tq_kernel_name(2, M, N, K)
     return tq.tq_kernel_name(2 if fmt == "tq2" else 1, M, N, K)
@@ -307,6 +328,137 @@ def context_bench(calls, per_call):
     return out
 
 
+def _time_graph(torch, launch, reps):
+    """Average µs of one launch: a captured graph of ``reps`` calls of
+    ``launch(i, stream)``, replayed once to warm up and once timed."""
+    stream = torch.cuda.current_stream()
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(reps):
+                launch(i, cap.cuda_stream)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) / reps * 1e3
+
+
+def _ring(torch, arrays, per_set):
+    """Device copies of ``arrays`` (numpy), enough sets for >= 1 GiB in all."""
+    R = max(2, -(-RING_BYTES // per_set))
+    first = [torch.from_numpy(a).cuda() for a in arrays]
+    return [first] + [[t.clone() for t in first] for _ in range(R - 1)]
+
+
+def _call_record(fmt, M, N, K, us, kernel):
+    b, f = alg_bytes(fmt, M, N, K), alg_flops(M, N, K)
+    return {"fmt": fmt, "M": M, "N": N, "K": K, "kernel": kernel, "us": round(us, 3),
+            "TBps": round(b / us / 1e6, 3), "TFLOPps": round(f / us / 1e6, 2),
+            "bound": "hbm" if b / HBM_PEAK >= f / MFMA_F16_PEAK else "mfma",
+            "roof_frac": round(t_roof(fmt, M, N, K) / (us * 1e-6), 4)}
+
+
+def _gemm_launcher(tq, fmt, M, N, K, X, Y, ring, ws=None):
+    def launch(i, sp):
+        q, sc = ring[i % len(ring)]
+        if fmt == "tq2":
+            st = tq.lib.tq_gemm_tq2(X.data_ptr(), q.data_ptr(), sc.data_ptr(), Y.data_ptr(), M, N,
+                                    K, sp)
+        elif ws is not None and M >= tq.tq_tq1_transcode_min_m(N, K):
+            st = tq.lib.tq_gemm_tq1_ws(X.data_ptr(), q.data_ptr(), q.shape[1], sc.data_ptr(),
+                                       Y.data_ptr(), M, N, K, ws.data_ptr(), ws.numel(), sp)
+        else:
+            st = tq.lib.tq_gemm_tq1(X.data_ptr(), q.data_ptr(), q.shape[1], sc.data_ptr(),
+                                    Y.data_ptr(), M, N, K, sp)
+        if st != 0:
+            raise RuntimeError(f"tq_gemm_{fmt} failed: {tq.tq_status_string(st)}")
+    return launch
+
+
+# The decode linears of a 3B-class layer at M = 1 (name, K, N), and the
+# 1024 x 1024 GEMV; weights ternarized from N(0, 0.02) latents (eps = 1e-5)
+# by the host packer, scales fp16(gamma).
+SMALL_LAYER = [("q", 3072, 3072), ("k", 3072, 3072), ("v", 3072, 3072), ("o", 3072, 3072),
+               ("gate", 3072, 8192), ("up", 3072, 8192), ("down", 8192, 3072)]
+
+
+def other_configs_bench(reps=30):
+    """µs per call of the 1024 x 1024 GEMV (M = 1) and of the seven decode
+    linears of a 3B-class layer (M = 1), both formats, latent-ternarized
+    weights rotating through >= 1 GiB like the sweep.  These calls are a few
+    µs or less, so launch cost dominates: reported as latency beside their
+    HBM fractions, not part of ``value``."""
+    import torch
+    import bit_mixed_precision_amd.binding as tq
+    from synth import activations_fp16, latent_weights_f32, seed_for
+    out = {"gemv_1024": [], "layer_3b_m1": []}
+    shapes = [("gemv_1024", "w", 1024, 1024)] + [("layer_3b_m1", n, K, N) for n, K, N in SMALL_LAYER]
+    for group, name, K, N in shapes:
+        W = latent_weights_f32(seed_for(900, K, N, len(name)), N, K, 0.02)
+        X = torch.from_numpy(activations_fp16(seed_for(901, 1, K), 1, K)).cuda()
+        Y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+        for fmt in ("tq2", "tq1"):
+            qs, sc, _ = (tq.tq_pack_tq2 if fmt == "tq2" else tq.tq_pack_tq1)(W, eps=1e-5)
+            ring = _ring(torch, [qs, sc], qs.nbytes + sc.nbytes)
+            us = _time_graph(torch, _gemm_launcher(tq, fmt, 1, N, K, X, Y, ring), reps)
+            rec = _call_record(fmt, 1, N, K, us, tq.tq_kernel_name(2 if fmt == "tq2" else 1, 1, N, K))
+            rec["linear"] = name
+            out[group].append(rec)
+            del ring
+    for fmt in ("tq2", "tq1"):
+        rows = [r for r in out["layer_3b_m1"] if r["fmt"] == fmt]
+        t = sum(r["us"] for r in rows)
+        b = sum(alg_bytes(fmt, 1, r["N"], r["K"]) for r in rows)
+        out[f"layer_3b_m1_{fmt}_total"] = {"us": round(t, 3), "TBps": round(b / t / 1e6, 3),
+                                           "hbm_frac": round(b / HBM_PEAK / (t * 1e-6), 4)}
+    return out
+
+
+TQ1_PS = [0.3, 0.5, 0.9]
+
+
+def tq1_vs_tq2_bench(reps=30):
+    """TQ1 against TQ2 on the same weights: for each zero fraction p, one i.i.d.
+    trit matrix and one scale table per shape, packed both ways, timed at
+    M in {1, 4, 16, 64} exactly as the step times its calls (TQ1 through the
+    workspace product from its switch point on)."""
+    import torch
+    import bit_mixed_precision_amd.binding as tq
+    from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
+    rows = []
+    for K, N in SHAPES:
+        xs = {M: torch.from_numpy(activations_fp16(seed_for(902, M, K), M, K)).cuda()
+              for M in TQ1_MS}
+        ys = {M: torch.empty((M, N), dtype=torch.float16, device="cuda") for M in TQ1_MS}
+        ws = torch.empty(N * K // 4, dtype=torch.uint8, device="cuda")
+        for p in TQ1_PS:
+            rng = seed_for(903, N, K, int(p * 100))
+            T = ternary_iid(rng, N, K, p)
+            s = block_scales_fp16(rng, N, K)
+            packed = {"tq2": tq.tq_pack_tq2(T)[0], "tq1": tq.tq_pack_tq1(T)[0]}
+            del T
+            us = {}
+            for fmt, qs in packed.items():
+                ring = _ring(torch, [qs, s], qs.nbytes + s.nbytes)
+                for M in TQ1_MS:
+                    us[(fmt, M)] = _time_graph(
+                        torch, _gemm_launcher(tq, fmt, M, N, K, xs[M], ys[M], ring, ws), reps)
+                del ring
+            for M in TQ1_MS:
+                r1, r2 = (_call_record(f, M, N, K, us[(f, M)], kernel_label(tq, f, M, N, K))
+                          for f in ("tq1", "tq2"))
+                rows.append({"p": p, "M": M, "N": N, "K": K, "tq1": r1, "tq2": r2,
+                             "tq1_over_tq2_time": round(r1["us"] / r2["us"], 3)})
+            log(f"[bench] tq1 vs tq2 N={N} p={p} done")
+    return rows
+
+
 def kernel_source_sha():
     """sha256 (first 16 hex) over the kernel sources, as recorded with the counters."""
     import glob
@@ -361,10 +513,49 @@ def roofline_of(per_call):
 
 # ----------------------------------------------------------------------------- CPU baseline
 
-def cpu_baseline(calls, cols=1024):
+def cpu_model():
+    """The host CPU's model name (lscpu, else /proc/cpuinfo), or None."""
+    import subprocess
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(calls, cols=1024, single_thread_cols=128):
     """The fp64 oracle on the host: each call of the step on ``cols`` sampled
-    output columns, time scaled by N / cols."""
-    from oracle import gemm_bwd_x_ref, gemm_ref
+    output columns, time scaled by N / cols, with every BLAS thread; then the
+    same on ``single_thread_cols`` columns with BLAS limited to one thread."""
+    res = _cpu_baseline_run(calls, cols)
+    single_thread_cols = min(cols, single_thread_cols)
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            one = _cpu_baseline_run(calls, single_thread_cols)
+        res["single_thread"] = {"value": one["value"], "cores": 1, "s_per_step": one["s_per_step"],
+                                "sample": f"every call on {single_thread_cols} sampled output "
+                                          f"columns, BLAS limited to one thread, time scaled "
+                                          f"by N/{single_thread_cols}"}
+    except ImportError:  # pragma: no cover
+        res["single_thread"] = None
+    res["cpu_model"] = cpu_model()
+    res["host_cpus"] = os.cpu_count()
+    return res
+
+
+def _cpu_baseline_run(calls, cols):
+    from oracle import gemm_bwd_x_ref, gemm_ref, ste_grad_w_ref
     from synth import activations_fp16, block_scales_fp16, seed_for, ternary_iid
     try:
         from threadpoolctl import threadpool_info
@@ -374,7 +565,13 @@ def cpu_baseline(calls, cols=1024):
     weights = {}
     total_t = total_roof = total_bytes = total_flops = 0.0
     for fmt, M, N, K in calls:
-        if fmt == "bwd":  # dX on `cols` sampled columns k: the full N x cols weight slice
+        if fmt == "ste":  # dW on `cols` sampled rows n
+            dY = activations_fp16(seed_for(604, M, cols), M, cols)
+            X = activations_fp16(seed_for(605, M, K), M, K)
+            t = time.perf_counter()
+            ste_grad_w_ref(dY, X)
+            dt = (time.perf_counter() - t) * (N / cols)
+        elif fmt == "bwd":  # dX on `cols` sampled columns k: the full N x cols weight slice
             rng = seed_for(602, N, K)
             T = ternary_iid(rng, N, 256, 0.31)
             s = block_scales_fp16(rng, N, 256)
@@ -612,6 +809,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the read-ceiling and FP16-matmul context of the sweep")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the timing of the 1024 x 1024 GEMV, the 3B-class layer and the "
+                         "TQ1-vs-TQ2 zero-fraction sweep")
     ap.add_argument("--calls-out", default=None, help="also write the per-call table here (JSON)")
     ap.add_argument("--bwd", action="store_true",
                     help="QAT backward dX = dY (s.T) at the 70B layer shapes, 4096 tokens")
@@ -680,16 +880,17 @@ def main():
     value = roof_sum / (ms_step * 1e-3)
     if args.bwd:
         out = {
-            "metric": "QAT backward dX = dY (s.T) TFLOP/s vs FP16 MFMA peak, 70B layer shapes at "
-                      "4096 tokens",
+            "metric": "QAT backward dX = dY (s.T) and straight-through dW = dY^T X TFLOP/s vs "
+                      "FP16 MFMA peak, 70B layer shapes at 4096 tokens",
             "value": round(value, 4),
             "unit": "fraction of roofline (FP16 MFMA 2.5 PFLOP/s; every call is MFMA-bound)",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(ms_step, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "f16", "data": "synthetic",
-            "config": {"workload": "dX for (N,K) in {(8192,8192),(28672,8192),(8192,28672)}, "
-                                   "M=4096 tokens; i.i.d. trits, fp16 block scales",
+            "config": {"workload": "dX and dW for (N,K) in {(8192,8192),(28672,8192),"
+                                   "(8192,28672)}, M=4096 tokens; i.i.d. trits, fp16 block "
+                                   "scales; dW fp32",
                        "global_batch": None, "seq_len": None, "parallelism": "none"},
             "roofline": roofline_of(per_call),
             "tflops_total": round(sum(alg_flops(*c[1:]) for c in calls) / (ms_step * 1e-3) / 1e12,
@@ -698,8 +899,9 @@ def main():
         if not args.no_cpu_baseline:
             log("[bench] CPU baseline (oracle) ...")
             cb = cpu_baseline(calls)
-            cb["sample"] = "every call on 256 sampled columns k (the full N x 256 weight slice, fp64 " \
-                           "dequantize + numpy matmul), time scaled by K/256"
+            cb["sample"] = "dX: every call on 256 sampled columns k (the full N x 256 weight " \
+                           "slice, fp64 dequantize + numpy matmul), time scaled by K/256; dW: " \
+                           "1024 sampled rows n, time scaled by N/1024"
             out["cpu_baseline"] = cb
         out["calls"] = per_call
         print(json.dumps(out), flush=True)
@@ -747,6 +949,10 @@ def main():
     if not args.no_context:
         log("[bench] context: read ceiling and FP16 matmul ...")
         out["context"] = context_bench(calls, per_call)
+    if not args.no_configs:
+        log("[bench] other workloads: 1024 x 1024 GEMV, 3B-class layer, TQ1 vs TQ2 ...")
+        out["other_configs"] = other_configs_bench()
+        out["tq1_vs_tq2_same_weights"] = tq1_vs_tq2_bench()
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle) ...")
         out["cpu_baseline"] = cpu_baseline(calls)

@@ -63,6 +63,7 @@ SIGNATURES = {
     "tq_gemm_tq2_swiglu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_gemm_tq2_bwd_x": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_stream_read": (_I, [_P, _I64, _P, _P]),
+    "tq_ste_grad_w": (_I, [_P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "tq_transcode_tq1_tq2": (_I, [_P, _I64, _I64, _I64, _P, _P]),
     "tq_tq1_transcode_min_m": (_I64, [_I64, _I64]),
     "tq_gemm_tq1_ws": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
@@ -331,6 +332,31 @@ def tq_gemm_tq2_bwd_x(dY, qs, scales, dX=None, stream=None):
         _check(lib.tq_gemm_tq2_bwd_x(_ptr(dY), _ptr(qs), _ptr(scales), _ptr(dX), M, N, K,
                                      _stream(stream, dY.device)), where)
     return dX
+
+
+def tq_ste_grad_w(dY, X, dW=None, accumulate: bool = False, stream=None):
+    """Latent-weight gradient under the straight-through estimator: dW [N][K]
+    (float32) = dY^T X, or dW + dY^T X with accumulate (dW then required);
+    dY fp16 [M][N], X fp16 [M][K]."""
+    import torch
+    where = "tq_ste_grad_w"
+    M, N = _rank2(dY, "dY", where)
+    M2, K = _rank2(X, "X", where)
+    if M2 != M:
+        raise TQError(TQ_ERR_SHAPE, f"{where}: dY has {M} rows, X {M2}")
+    _need(dY, "dY", "f16", None, where)
+    _need(X, "X", "f16", None, where)
+    if dW is not None:
+        _need(dW, "dW", "f32", (N, K), where)
+    elif accumulate:
+        raise TQError(TQ_ERR_NULL, f"{where}: accumulate needs dW")
+    _on_gpu(where, ("dY", dY), ("X", X), ("dW", dW))
+    if dW is None:
+        dW = torch.empty((N, K), dtype=torch.float32, device=dY.device)
+    with _device_of(dY):
+        _check(lib.tq_ste_grad_w(_ptr(dY), _ptr(X), _ptr(dW), M, N, K, int(bool(accumulate)),
+                                 _stream(stream, dY.device)), where)
+    return dW
 
 
 def tq_tq1_transcode_min_m(N: int, K: int) -> int:

@@ -17,6 +17,9 @@ constexpr int64_t kMaxBwdN = int64_t(1) << 20;  // 32-bit offsets in 512 rows of
 // Largest TQ1 row stride: the kernels take it as a 32-bit int and form byte
 // offsets such as 16 rows * ldq inside a workgroup in 32 bits.
 constexpr int64_t kMaxLdq = int64_t(1) << 24;
+// Largest dY and X of the weight gradient, in elements: 2 GiB of fp16 each,
+// so that every byte offset fits the kernel's 32-bit buffer offsets.
+constexpr int64_t kMaxSteElems = int64_t(1) << 30;
 // Activation rows from which a TQ1 product with a workspace transcodes the
 // weights once and runs the TQ2 kernels.  The TQ1 kernels cost a step per 16
 // (skinny) or 32 rows (two slices); the transcoding a fixed read and write of
@@ -251,6 +254,22 @@ int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales, void* 
   int st = device_ready();
   if (st != TQ_OK) return st;
   return finish(tq::launch_tq2_bwd_x(dY, qs, scales, dX, M, N, K, static_cast<hipStream_t>(stream)));
+}
+
+int tq_ste_grad_w(const void* dY, const void* X, float* dW, int64_t M, int64_t N, int64_t K,
+                  int accumulate, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return TQ_ERR_SHAPE;
+  if (N == 0 || K == 0 || (M == 0 && accumulate == 1)) return TQ_OK;
+  if (!dW || (M > 0 && (!dY || !X))) return TQ_ERR_NULL;  // M = 0 reads neither input
+  if (N % 8 || K % 8 || N > kMaxMN || K > kMaxMN || M * N > kMaxSteElems ||
+      M * K > kMaxSteElems)
+    return TQ_ERR_SHAPE;
+  if (!aligned16(dY) || !aligned16(X) || !aligned16(dW)) return TQ_ERR_ALIGN;
+  if (accumulate != 0 && accumulate != 1) return TQ_ERR_VALUE;
+  int st = device_ready();
+  if (st != TQ_OK) return st;
+  return finish(tq::launch_ste_grad_w(dY, X, dW, M, N, K, accumulate,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int tq_stream_read(const void* src, int64_t bytes, void* sink, void* stream) {

@@ -47,6 +47,12 @@ int glu_rows(int64_t N);
 hipError_t launch_tq2_bwd_x(const void* dY, const void* qs, const void* scales, void* dX,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// Latent-weight gradient under the straight-through estimator:
+// dW [N][K] (fp32) = dY^T X (+ dW when accumulate), dY [M][N], X [M][K] fp16,
+// N and K multiples of 8, M N and M K at most 2^30.
+hipError_t launch_ste_grad_w(const void* dY, const void* X, float* dW, int64_t M, int64_t N,
+                             int64_t K, int accumulate, hipStream_t stream);
+
 // TQ1 MFMA kernel: any M, in slices of 16 activation rows.
 hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream);
 int tq1_depth();

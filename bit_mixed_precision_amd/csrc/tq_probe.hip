@@ -7,9 +7,13 @@
 // every byte once with the same 16-byte non-temporal loads and writes nothing
 // (unless the folded data equals one fixed value, which keeps the loads alive).
 //
-// MI355X shape: 256 workgroups (one per CU) of 512 threads, each streaming a
-// contiguous slice four loads deep; the best of a sweep of grid and block
-// shapes for 17 MB and 60 MB buffers.
+// MI355X shape: workgroups of 1024 threads, each streaming a contiguous slice
+// two 16-byte loads deep per thread; 256 workgroups (one per CU) up to 32 MiB,
+// 2048 above.  A sweep of grids (256 .. 4096), block sizes (256 .. 1024) and
+// depths (2 .. 8), timed as back-to-back launches over >= 1 GiB of rotating
+// buffers, put these among the fastest for both sizes of an M = 1 call:
+// 17.3 MB in 4.34 us and 60.6 MB in 10.33 us (the earlier 256 x 512 x 4 shape:
+// 4.91 and 12.80 us).
 
 #include "tq_common.h"
 #include "tq_kernels.h"
@@ -18,8 +22,9 @@
 namespace tq {
 namespace {
 
-constexpr int kReadThreads = 512;
-constexpr int kReadDepth = 4;
+constexpr int kReadThreads = 1024;
+constexpr int kReadDepth = 2;
+constexpr int64_t kSmallReadBytes = int64_t(32) << 20;
 constexpr uint32_t kSinkMagic = 0x9E3779B9u;
 
 __global__ __launch_bounds__(kReadThreads) void tq_stream_read_kernel(const u32x4* __restrict__ p,
@@ -47,7 +52,8 @@ __global__ __launch_bounds__(kReadThreads) void tq_stream_read_kernel(const u32x
 }  // namespace
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, void* sink, hipStream_t stream) {
-  hipLaunchKernelGGL(tq_stream_read_kernel, dim3(256), dim3(kReadThreads), 0, stream,
+  const unsigned grid = bytes <= kSmallReadBytes ? 256u : 2048u;
+  hipLaunchKernelGGL(tq_stream_read_kernel, dim3(grid), dim3(kReadThreads), 0, stream,
                      static_cast<const u32x4*>(src), bytes / 16, static_cast<uint32_t*>(sink));
   return hipGetLastError();
 }

@@ -217,8 +217,11 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   u32x4 wbuf[D];
   uint16_t sbuf[D];
 
+  // Weights are read once: non-temporal loads (measured 3-5% faster at
+  // M <= 8 on both layer shapes than plain loads; the TQ1 kernel's 8-byte
+  // loads were slower with the hint, so it keeps plain ones).
   auto load = [&](int d, int b) {
-    wbuf[d] = *reinterpret_cast<const u32x4*>(wrow + 64 * b);
+    wbuf[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + 64 * b));
     if constexpr (!STAGE) sbuf[d] = srow[b];
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is
   };

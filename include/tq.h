@@ -219,10 +219,32 @@ int tq_gemm_tq2_swiglu(const void* X, const void* qs_gate, const void* scales_ga
  * a multiple of 256 (TQ_ERR_SHAPE otherwise); M = 0 is a no-op returning
  * TQ_OK.  Block scales must satisfy |s| < 1024: the kernel carries a column's
  * field position as an exact factor of up to 64 on the decoded s.  The weight
- * gradient under the straight-through estimator, dY^T X, is a plain dense
- * product left to the caller's BLAS. */
+ * gradient under the straight-through estimator is tq_ste_grad_w. */
 int tq_gemm_tq2_bwd_x(const void* dY, const void* qs, const void* scales_f16, void* dX,
                       int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Gradient that reaches the latent weights of a ternary linear under the
+ * straight-through estimator (project page "Scaling Laws and Efficient
+ * Inference for Ternary Language Models", "The model": gradients pass to the
+ * latent weights with a straight-through estimator; Spectra page,
+ * "Architecture of TriLM and FloatLM").  The quantizer W -> gamma T is taken
+ * as the identity in the backward pass, so the latent weights receive the
+ * gradient with respect to the effective weights of Y = X (gamma T)^T:
+ *   dW[n][k] = sum_m dY[m][n] * X[m][k]            (accumulate = 0)
+ *   dW[n][k] = dW[n][k] + sum_m dY[m][n] X[m][k]   (accumulate = 1)
+ * gamma is not differentiated and no weight is masked (e.g. outside the clip
+ * window |W / gamma| <= 1); the result does not depend on W, gamma or T.
+ * dY fp16 [M][N] (the output gradient), X fp16 [M][K] (the layer input), dW
+ * fp32 [N][K] (the latent weights' layout), all row-major device pointers,
+ * 16-byte aligned, owned by the caller; FP32 accumulation, FP32 output, the
+ * same bits on every run.  Shapes: M >= 0 (M = 0 writes zeros and reads
+ * neither input, which may then be NULL, or is a no-op with accumulate = 1);
+ * N = 0 or K = 0 is a no-op; N and K multiples of 8 and
+ * at most 2^24; M N and M K at most 2^30 (split larger batches and
+ * accumulate).  Errors: TQ_ERR_SHAPE, TQ_ERR_NULL, TQ_ERR_ALIGN,
+ * TQ_ERR_VALUE (accumulate not 0 or 1), TQ_ERR_DEVICE. */
+int tq_ste_grad_w(const void* dY, const void* X, float* dW, int64_t M, int64_t N, int64_t K,
+                  int accumulate, void* stream);
 
 /* Re-pack TQ1 weights as TQ2 on the device: the trits of qs1 ([N][ldq],
  * "1.6 bits per weight" on the project page "Scaling Laws and Efficient

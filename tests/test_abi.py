@@ -337,3 +337,37 @@ def test_binding_rejects_bad_other_tensors():
     _raises(tq.TQ_ERR_DEVICE, tq.tq_pack_dev, 2, _t((32, 512), "float32"))
     _raises(tq.TQ_ERR_VALUE, tq.tq_stream_read, _t((64,), "uint8"), _t((4,), "float32"))
     _raises(tq.TQ_ERR_DEVICE, tq.tq_stream_read, _t((64,), "uint8"), _t((4,), "int32"))
+
+
+def _sg_w(dY=A, X=A, dW=A, M=64, N=64, K=64, acc=0):
+    return tq.raw_call("tq_ste_grad_w", dY, X, dW, M, N, K, acc, None)
+
+
+def test_ste_grad_w_argument_errors():
+    """Shape, null, alignment and value checks before any device work; the
+    documented no-ops touch no pointer."""
+    assert _sg_w(dY=None, X=None, dW=None, N=0) == tq.TQ_OK
+    assert _sg_w(dY=None, X=None, dW=None, K=0) == tq.TQ_OK
+    assert _sg_w(dY=None, X=None, dW=None, M=0, acc=1) == tq.TQ_OK
+    assert _sg_w(M=-1) == tq.TQ_ERR_SHAPE
+    assert _sg_w(dW=None) == tq.TQ_ERR_NULL
+    assert _sg_w(X=None) == tq.TQ_ERR_NULL
+    assert _sg_w(dY=None, X=None, M=0, K=300) == tq.TQ_ERR_SHAPE  # M = 0 needs no inputs
+    assert _sg_w(N=60) == tq.TQ_ERR_SHAPE
+    assert _sg_w(K=12) == tq.TQ_ERR_SHAPE
+    assert _sg_w(M=1 << 20, N=2048) == tq.TQ_ERR_SHAPE   # M N past 2^30
+    assert _sg_w(M=1 << 20, K=2048) == tq.TQ_ERR_SHAPE
+    assert _sg_w(N=(1 << 24) + 8, M=1) == tq.TQ_ERR_SHAPE
+    assert _sg_w(X=A + 8) == tq.TQ_ERR_ALIGN
+    assert _sg_w(dW=A + 4) == tq.TQ_ERR_ALIGN
+    assert _sg_w(acc=2) == tq.TQ_ERR_VALUE
+
+
+def test_binding_rejects_bad_ste_tensors():
+    dY, X = _t((8, 64), "float16"), _t((8, 128), "float16")
+    _raises(tq.TQ_ERR_DEVICE, tq.tq_ste_grad_w, dY, X)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_ste_grad_w, dY, _t((9, 128), "float16"))
+    _raises(tq.TQ_ERR_VALUE, tq.tq_ste_grad_w, dY.float(), X)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_ste_grad_w, dY, X, _t((64, 64), "float32"))
+    _raises(tq.TQ_ERR_VALUE, tq.tq_ste_grad_w, dY, X, _t((64, 128), "float16"))
+    _raises(tq.TQ_ERR_NULL, tq.tq_ste_grad_w, dY, X, None, True)

@@ -702,7 +702,7 @@ def test_stream_read_covers_every_piece():
     """The read-ceiling kernel folds every 16-byte piece: a lone piece whose
     dwords XOR to the marker is found wherever it sits; zeros write nothing."""
     marker = 0x9E3779B9 - (1 << 32)  # as int32
-    n = (1 << 20) + 48  # not a multiple of the 256 x 512 x 4 pieces of one sweep
+    n = (1 << 20) + 48  # not a multiple of the pieces one pass of the grid reads
     src = torch.zeros(n // 4, dtype=torch.int32, device="cuda")
     sink = torch.full((4,), 7, dtype=torch.int32, device="cuda")
     tq.tq_stream_read(src, sink)
