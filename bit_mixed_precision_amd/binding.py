@@ -71,6 +71,7 @@ SIGNATURES = {
     "tq_pack_dev_workspace_bytes": (_I64, [_I64, _I64]),
     "tq_pack_tq2_dev": (_I, [_P, _I64, _I64, C.c_double, _P, _P, _P, _P, _P, _I64, _P]),
     "tq_pack_tq1_dev": (_I, [_P, _I64, _I64, C.c_double, _I64, _P, _P, _P, _P, _P, _I64, _P]),
+    "tq_pack_tq2_dev_noalloc": (_I, [_P, _I64, _I64, C.c_double, _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -474,6 +475,28 @@ def tq_pack_dev(fmt: int, W, eps: float = 1e-5, ldq: int | None = None, stream=N
                                      _ptr(gamma), _ptr(status), _ptr(ws), wsb, sp)
     _check(st, where)
     return qs, scales, gamma, status
+
+
+def tq_pack_tq2_dev_noalloc(W, qs, scales, gamma, status, eps: float = 1e-5, stream=None):
+    """tq_pack_tq2_dev into caller-owned outputs with the library's fixed
+    per-device workspace (no device allocation by this call): W float32
+    [N][K], qs uint8 [N][K/4], scales fp16 [N][K/256], gamma float64 [1],
+    status int32 [1], all on one GPU."""
+    import torch
+    where = "tq_pack_tq2_dev_noalloc"
+    N, K = _rank2(W, "W", where)
+    _need(W, "W", "f32", None, where)
+    _need(qs, "qs", "u8", (N, K // 4), where)
+    _need(scales, "scales", "f16", (N, K // 256), where)
+    if not (torch.is_tensor(gamma) and gamma.dtype == torch.float64 and gamma.numel() >= 1):
+        raise TQError(TQ_ERR_VALUE, f"{where}: gamma must be a float64 tensor of >= 1 element")
+    if not (torch.is_tensor(status) and status.dtype == torch.int32 and status.numel() >= 1):
+        raise TQError(TQ_ERR_VALUE, f"{where}: status must be an int32 tensor of >= 1 element")
+    _on_gpu(where, ("W", W), ("qs", qs), ("scales", scales), ("gamma", gamma), ("status", status))
+    with _device_of(W):
+        _check(lib.tq_pack_tq2_dev_noalloc(_ptr(W), N, K, float(eps), _ptr(qs), _ptr(scales),
+                                           _ptr(gamma), _ptr(status), _stream(stream, W.device)),
+               where)
 
 
 def tq_gemm_tq2(X, qs, scales, Y=None, stream=None):

@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tq.h"
 #include "tq_common.h"
 
@@ -366,9 +368,58 @@ int pack_grid(int64_t items) {
   return (int)(g < 1 ? 1 : g);
 }
 
+// The workspace of tq_pack_tq2_dev_noalloc: one fixed array per device,
+// reserved when the library is loaded and held until the process ends.  Host
+// code never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol); the device address comes from
+// hipGetSymbolAddress, once per device, kept in scratch_addr.
+constexpr int64_t kScratchBytes = kWorkspace;
+static_assert(kScratchBytes % 16 == 0, "scratch keeps the workspace's 16-byte alignment");
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<unsigned char*> scratch_addr[kMaxDevices];
+
+// Device address of the current device's scratch array (looked up on the
+// first call on each device; concurrent first calls store the same value).
+int scratch_on_current_device(unsigned char** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return TQ_ERR_DEVICE;
+  }
+  unsigned char* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess || !a) {
+      (void)hipGetLastError();
+      return TQ_ERR_DEVICE;
+    }
+    p = static_cast<unsigned char*>(a);
+    scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return TQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int tq_pack_tq2_dev_noalloc(const float* W, int64_t N, int64_t K, double eps, uint8_t* qs,
+                            uint16_t* scales, double* gamma, int* status, void* stream) {
+  // same checks as tq_pack_tq2_dev, with the fixed scratch as the workspace
+  if (!W || !qs || !scales) return TQ_ERR_NULL;
+  if (N < 1 || K < 256 || K % 256 || N > (int64_t(1) << 24) || K > (int64_t(1) << 20))
+    return TQ_ERR_SHAPE;
+  if (tq_pack_dev_workspace_bytes(N, K) > kScratchBytes) return TQ_ERR_SHAPE;
+  if (((uintptr_t)W | (uintptr_t)qs | (uintptr_t)scales) & 15) return TQ_ERR_ALIGN;
+  if (have_device() != TQ_OK) return TQ_ERR_DEVICE;
+  unsigned char* ws = nullptr;
+  const int st = scratch_on_current_device(&ws);
+  if (st != TQ_OK) return st;
+  return tq_pack_tq2_dev(W, N, K, eps, qs, scales, gamma, status, ws, kScratchBytes, stream);
+}
 
 int64_t tq_pack_dev_workspace_bytes(int64_t N, int64_t K) {
   if (N < 1 || K < 256 || K % 256) return -1;

@@ -182,6 +182,22 @@ int tq_pack_tq1_dev(const float* W, int64_t N, int64_t K, double eps, int64_t ld
                     uint16_t* scales_f16, double* gamma, int* status, void* workspace,
                     int64_t workspace_bytes, void* stream);
 
+/* tq_pack_tq2_dev without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc).  It runs the same four kernels with the
+ * workspace in a fixed array of the library, tq_pack_dev_workspace_bytes()
+ * bytes (4224) per device, reserved when the library is loaded and held until
+ * the process ends; no call allocates or frees anything.  Every call on a
+ * device uses that device's one array, so calls that overlap in time on one
+ * device (other streams, other host threads) race and give unspecified qs,
+ * scales and gamma; calls in one stream's order do not (each clears the
+ * totals it needs at its start).  Arguments, results, status and errors as
+ * tq_pack_tq2_dev (the same shape limits: N <= 2^24, K <= 2^20; a shape whose
+ * workspace would exceed the array gives TQ_ERR_SHAPE); TQ_ERR_DEVICE also
+ * when the array's device address cannot be obtained. */
+int tq_pack_tq2_dev_noalloc(const float* W, int64_t N, int64_t K, double eps, uint8_t* qs,
+                            uint16_t* scales_f16, double* gamma, int* status, void* stream);
+
 /* TQ2 product on the tiled kernel with an explicit tile, for tuning and for
  * tests of every tile: 16 mt activation rows x 64 ng weight rows (32 ng when
  * mt = 8) per workgroup of ng x kg waves (kg of them split K).  Compiled
