@@ -60,6 +60,7 @@ SIGNATURES = {
     "tq_gemm_tq1_ex": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _P]),
     "tq_gemm_tq2_tiled": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_gemm_tq2_tile": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P]),
+    "tq_gemm_tq2_wide": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P]),
     "tq_gemm_tq2_swiglu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_gemm_tq2_bwd_x": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "tq_stream_read": (_I, [_P, _I64, _P, _P]),
@@ -427,6 +428,17 @@ def tq_gemm_tq2_tile(X, qs, scales, mt: int, nr: int, ng: int, kg: int, Y=None, 
     Y = _out(Y, M, N, where, (("X", X), ("qs", qs), ("scales", scales)))
     with _device_of(X):
         _check(lib.tq_gemm_tq2_tile(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, nr, ng,
+                                    kg, _stream(stream, X.device)), where)
+    return Y
+
+
+def tq_gemm_tq2_wide(X, qs, scales, mt: int, nt: int, ng: int, kg: int, Y=None, stream=None):
+    """tq_gemm_tq2 on the wide-tile kernel with an explicit (mt, nt, ng, kg) tile."""
+    where = "tq_gemm_tq2_wide"
+    M, N, K, _ = _gemm_operands(X, qs, scales, where)
+    Y = _out(Y, M, N, where, (("X", X), ("qs", qs), ("scales", scales)))
+    with _device_of(X):
+        _check(lib.tq_gemm_tq2_wide(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, nt, ng,
                                     kg, _stream(stream, X.device)), where)
     return Y
 

@@ -69,6 +69,16 @@ bool tiled_compiled(const TiledShape& t);  // one of the instantiated tiles
 hipError_t launch_tq2_tiled(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_tq2_tiled_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream);
 
+// Wide-tile MFMA kernel (v_mfma_f32_32x32x16_f16): a workgroup of 4 waves
+// (ng weight-row groups x kg k-groups) owns 32 mt activation rows x 32 nt ng
+// weight rows.
+struct WideShape {
+  int mt, nt, ng, kg;
+};
+bool wide_compiled(const WideShape& w);
+bool wide_fits(int64_t M, int64_t N, int64_t K);  // 32-bit buffer offsets suffice
+hipError_t launch_tq2_wide_shape(const WideShape& w, const GemmArgs& a, hipStream_t stream);
+
 // Tiled MFMA kernel for TQ1 and M > 16: a workgroup of nw x kg waves (kg of
 // them split K) owns 16 mt activation rows x 16 nw weight rows.
 struct Tq1TiledShape {

@@ -50,45 +50,6 @@ __device__ __forceinline__ void sfor(F&& f) {
 // s_waitcnt immediate that waits for the vector-memory counter only.
 constexpr int vmcnt_imm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
-// Natural-order decode constants: the low half takes field 2q of a byte, the
-// high half field 2q + 1 (q = 0, 1).
-struct NaturalConsts {
-  uint32_t magic;
-  uint32_t mul[2], add[2];
-  __device__ __forceinline__ void init() {
-    magic = in_vgpr(kMagic2);
-    mul[0] = in_vgpr(pack_half2(1.0f, 0.25f));
-    add[0] = in_vgpr(pack_half2(-1025.0f, -257.0f));
-    mul[1] = in_vgpr(pack_half2(1.0f / 16.0f, 1.0f / 64.0f));
-    add[1] = in_vgpr(pack_half2(-65.0f, -17.0f));
-  }
-  // z holds one weight byte in the low byte of both halves; returns the fp16
-  // pair (s * d_{2q}, s * d_{2q+1}) for q = Q.
-  template <int Q>
-  __device__ __forceinline__ uint32_t pair(uint32_t z, uint32_t s2) const {
-    constexpr uint32_t mask = Q == 0 ? 0x000C0003u : 0x00C00030u;
-    const uint32_t v = (z & mask) | magic;
-    const half2v d = __builtin_elementwise_fma(__builtin_bit_cast(half2v, v),
-                                               __builtin_bit_cast(half2v, mul[Q]),
-                                               __builtin_bit_cast(half2v, add[Q]));
-    return __builtin_bit_cast(uint32_t, d * __builtin_bit_cast(half2v, s2));
-  }
-  // B operand of 8 consecutive weights: the byte pair H (0 or 1) of dword x,
-  // times the scale pair s2.
-  template <int H>
-  __device__ __forceinline__ half8 operand(uint32_t x, uint32_t s2) const {
-    // both halves hold bytes (2H, 2H + 1): [b, b', b, b']
-    const uint32_t z = perm(x, x, H == 0 ? 0x01000100u : 0x03020302u);
-    const uint32_t z2 = z >> 8;  // low byte of each half = b'
-    u32x4 r;
-    r[0] = pair<0>(z, s2);
-    r[1] = pair<1>(z, s2);
-    r[2] = pair<0>(z2, s2);
-    r[3] = pair<1>(z2, s2);
-    return __builtin_bit_cast(half8, r);
-  }
-};
-
 // Lane (n, g) holds bytes 16 g .. 16 g + 15 of row n's 64-byte block.  In the
 // MFMA B order lane (n, g) needs, for step j = 0..7 (32 weights each), the
 // bytes 8 j + 2 g and 8 j + 2 g + 1 (weights 32 j + 8 g .. + 7).  Returns

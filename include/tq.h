@@ -315,6 +315,16 @@ int tq_stream_read(const void* src, int64_t bytes, void* sink, void* stream);
 int tq_gemm_tq2_tile(const void* X, const void* qs, const void* scales_f16, void* Y, int64_t M,
                      int64_t N, int64_t K, int mt, int nr, int ng, int kg, void* stream);
 
+/* TQ2 product on the wide-tile kernel (v_mfma_f32_32x32x16_f16) with an
+ * explicit tile, for tuning and for tests of every tile: 32 mt activation rows
+ * x 32 nt ng weight rows per workgroup of ng x kg = 4 waves (kg of them split
+ * K).  Compiled tiles: mt in {1, 2, 4}, nt in {1, 2}, (ng, kg) in {(2, 2),
+ * (1, 4)}, except mt = 4 with kg = 4; any other gives TQ_ERR_UNSUPPORTED.
+ * M K and N K / 4 must stay below 2^31 bytes (TQ_ERR_SHAPE otherwise).
+ * Everything else is as tq_gemm_tq2. */
+int tq_gemm_tq2_wide(const void* X, const void* qs, const void* scales_f16, void* Y, int64_t M,
+                     int64_t N, int64_t K, int mt, int nt, int ng, int kg, void* stream);
+
 /* TQ1 product on the tiled kernel with an explicit tile, for tuning and for
  * tests of every tile: 16 mt activation rows x 16 nw weight rows per
  * workgroup of nw x kg waves (kg of them split K).  Compiled tiles: (mt, nw,

@@ -152,6 +152,45 @@ def test_every_tiled_tile(mt, nr, ng, kg, M, N, K):
         check_close(Y.cpu().numpy(), ref(X, T, s), f"tiled {mt},{ng},{kg} {M}x{N}x{K}")
 
 
+WIDE_TILES = [(mt, nt, 2, 2) for mt in (1, 2, 4) for nt in (1, 2)]
+WIDE_TILES += [(mt, nt, 1, 4) for mt in (1, 2) for nt in (1, 2)]
+# ragged in M and N against the 32-row blocks and the tiles; K / 256 = 1 .. 5
+# (one stage to several), M = 1 (one real row in a 32-row block)
+WIDE_SHAPES = [(1, 64, 256), (17, 100, 256), (40, 300, 768), (64, 257, 1024),
+               (100, 520, 1280), (130, 1000, 512)]
+
+
+@pytest.mark.parametrize("mt,nt,ng,kg", WIDE_TILES)
+@pytest.mark.parametrize("M,N,K", WIDE_SHAPES)
+def test_every_wide_tile(mt, nt, ng, kg, M, N, K):
+    """Each compiled tile of the wide-tile (32 x 32 x 16 MFMA) kernel over
+    several tiles and ragged tails against the oracle."""
+    say(f"[wide] mt={mt} nt={nt} ng={ng} kg={kg} M={M} N={N} K={K}")
+    T, s = iid_problem(N, K, 0.31, 15)
+    X = activations(M, K, 15)
+    Y = torch.full((M, N), float("nan"), dtype=torch.float16, device="cuda")
+    tq.tq_gemm_tq2_wide(dev(X), dev(pack("tq2", T)), dev(s), mt, nt, ng, kg, Y)
+    torch.cuda.synchronize()
+    check_close(Y.cpu().numpy(), ref(X, T, s), f"wide {mt},{nt},{ng},{kg} {M}x{N}x{K}")
+
+
+def test_wide_exact_special_cases():
+    """The wide kernel decodes exact trits times the block scale: identity,
+    minus identity, a permutation and one weight per row give fp16 bits equal
+    to the exact product's rounding."""
+    K = 512
+    for tile in ((4, 2, 2, 2), (1, 1, 1, 4)):
+        X = activations(40, K, 16)
+        one = np.ones((K, K // 256), np.float16)
+        I = np.eye(K, dtype=np.int8)
+        for W, want in ((I, X), (-I, -X)):
+            Y = tq.tq_gemm_tq2_wide(dev(X), dev(pack("tq2", W)), dev(one), *tile).cpu().numpy()
+            assert np.array_equal(Y.astype(np.float64), want.astype(np.float64)), tile
+        perm = seed_for(17).permutation(K)
+        Y = tq.tq_gemm_tq2_wide(dev(X), dev(pack("tq2", I[perm])), dev(one), *tile).cpu().numpy()
+        assert np.array_equal(Y.view(np.uint16), X[:, perm].view(np.uint16)), tile
+
+
 TQ1_TILES = [(1, 4, 4), (2, 4, 2), (2, 4, 4), (4, 4, 1), (4, 4, 2), (2, 8, 2)]
 # ragged in M and N; K with 1, 3, 4, 5 blocks: spans with and without a block
 # boundary, a last span past ldq, ldq larger than ceil(K / 5)
