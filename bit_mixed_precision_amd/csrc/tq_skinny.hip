@@ -413,7 +413,12 @@ int skinny_lwk(int64_t N, int64_t K, int64_t M) {
   // groups per workgroup, fewer waves that each take at least 8 blocks beat
   // more waves (M = 4, N = K = 8192: 8 waves 8.6 us, 16 waves 9.4 us; with
   // one row group 8 waves of 4 blocks still win: N = 3072, 6.3 against 7.1).
-  const int64_t min_blocks = (M <= 2 || (M <= 4 && RG >= 2)) ? 8 : 1;
+  // On short rows (K < 8192) that leaves too few waves to cover the first
+  // loads' latency; there 2 blocks per wave (M = 1: K = N = 3072 6.45 ->
+  // 4.46 us, K = 3072, N = 8192 6.85 -> 5.09 us, K = N = 1024 3.47 -> 3.13 us;
+  // one block per wave was slower at K = 3072, N = 8192: 6.03 us).
+  const int64_t few = nb >= 32 ? 8 : 2;
+  const int64_t min_blocks = (M <= 2 || (M <= 4 && RG >= 2)) ? few : 1;
   int lwk = 0;
   while ((RG << (lwk + 1)) <= 16 && (min_blocks << (lwk + 1)) <= nb) ++lwk;
   return lwk;
@@ -464,7 +469,7 @@ int glu_rows(int64_t N) {
 int glu_lwk(int64_t N, int64_t K, int64_t M) {
   const int RG = 2 * glu_rows(N);
   const int64_t nb = K / 256;
-  const int64_t min_blocks = M <= 2 ? 8 : 1;
+  const int64_t min_blocks = M <= 2 ? (nb >= 32 ? 8 : 2) : 1;  // as skinny_lwk
   int lwk = 0;
   while ((RG << (lwk + 1)) <= 16 && (min_blocks << (lwk + 1)) <= nb) ++lwk;
   return lwk;
