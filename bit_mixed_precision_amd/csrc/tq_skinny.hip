@@ -60,13 +60,16 @@ __device__ __forceinline__ void static_for(F&& f) {
 // slot 2i / 2i+1 holds weight 64 g + 16 i + c / 64 g + 16 i + 8 + c, at field
 // position p = c % 4 of its half.  The matching A operand of class c is the
 // lane's activations x[64 g + 8 s + c], s = 0..7, times 1/4 for odd c, which
-// the LDS copy stores as 16 contiguous bytes: Xt[m][block][g][c][s].
+// the LDS copy stores as 16 contiguous bytes: Xt[m][block][g][c][s], the
+// blocks of a row kBlkStride bytes apart: the 512 bytes plus 32, so that the
+// eight staging units of a wave (neighbouring blocks of one row) write to
+// eight different groups of eight banks.
 // Chain of class c: 0 for p in {0, 1}, 1 for p in {2, 3}; a chain-0 product
 // is x d' 2^-24, a chain-1 product 16 x d' 2^-24.
 // ----------------------------------------------------------------------------
 
 constexpr int kXRowPad = 16;          // bytes between LDS rows of Xt (bank spread)
-constexpr int kXLdsMax = 132 * 1024;  // LDS budget of the activation window and its sums
+constexpr int kBlkStride = 512 + 32;  // bytes between the blocks of a row of Xt
 constexpr int kBiasBytes = 64;        // per block of the window: 16 fp32 row sums
 constexpr int kScaleLdsMax = 24 * 1024;
 constexpr int kLdsLimit = 160 * 1024;
@@ -125,13 +128,18 @@ __device__ __forceinline__ void piece_load(u32x4 (&v)[4], const uint16_t* __rest
 
 // Writes a unit's activations to their class slots (odd classes times 1/4)
 // and the block's negated row sum of the values the MFMAs see, times 2^-24.
+// Threads s and s ^ 1 (all lanes active) swap their pairs with one DPP move,
+// so that each writes a dword: the even one class 2 i at slots s, s + 1, the
+// odd one class 2 i + 1 at slots s - 1, s.
 __device__ __forceinline__ void piece_store(const u32x4 (&v)[4], bool ok, PiecePos p,
                                             unsigned char* xs, float* bias, unsigned char* trash,
                                             int xstride, int s) {
   const half2v quarter = {(_Float16)1.0f, (_Float16)0.25f};
   const half2v four = {(_Float16)1.0f, (_Float16)4.0f};
   float part = 0.f;
-  unsigned char* d = (ok ? xs + p.m * xstride + p.bw * 512 : trash) + 2 * s;
+  const int odd = s & 1;
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;  // (its hi, own hi) : (own lo, its lo)
+  unsigned char* d = (ok ? xs + p.m * xstride + p.bw * kBlkStride : trash) + 16 * odd + 2 * (s & ~1);
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
 #pragma unroll
@@ -141,8 +149,9 @@ __device__ __forceinline__ void piece_store(const u32x4 (&v)[4], bool ok, PieceP
       const half2v a = __builtin_bit_cast(half2v, xv) * quarter;
       part = __builtin_amdgcn_fdot2(a, four, part, false);
       const uint32_t ab = __builtin_bit_cast(uint32_t, a);
-      *reinterpret_cast<uint16_t*>(d + g * 128 + (2 * i) * 16) = (uint16_t)ab;
-      *reinterpret_cast<uint16_t*>(d + g * 128 + (2 * i + 1) * 16) = (uint16_t)(ab >> 16);
+      // quad_perm [1, 0, 3, 2]: the pair of thread s ^ 1
+      const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ab, 0xB1, 0xf, 0xf, false);
+      *reinterpret_cast<uint32_t*>(d + g * 128 + (2 * i) * 16) = perm(other, ab, sel);
     }
   }
   part += dpp_f32<0xB1>(part);   // quad_perm [1, 0, 3, 2]
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   const int rgo = up ? rg - RGO : rg;
   const int n_base = blockIdx.x * (16 * RGO);
   const int rows = min(16 * RGO, N - n_base);
-  const int xstride = nbw * 512 + kXRowPad;
+  const int xstride = nbw * kBlkStride + kXRowPad;
   const size_t row_bytes = (size_t)(K >> 2);
   float* bias = reinterpret_cast<float*>(smem + M * xstride);
   unsigned char* trash = reinterpret_cast<unsigned char*>(bias + 16 * nbw);
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
     const float sc = STAGE ? sc_lds[sc_row + b] : h2f(sbuf[d]);
     float4v c0 = *reinterpret_cast<const float4v*>(ba + 16 * bw);  // -2^-24 (row sums)
     float4v c1 = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* xb = xa + bw * 512;
+    const unsigned char* xb = xa + bw * kBlkStride;
     auto A = [&](int c) { return *reinterpret_cast<const half8*>(xb + 16 * c); };
     c0 = mfma16(A(0), tq2_class<0>(w, w8), c0);
     c1 = mfma16(A(2), tq2_class<2>(w, w8), c1);
@@ -245,85 +254,128 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
     for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, __builtin_fmaf(c1[i], 0.0625f, c0[i]), acc[i]);
   };
 
-  for (int wb0 = 0; wb0 < nb; wb0 += nbw) {
-    const int nbw_here = min(nbw, nb - wb0);
-    const int cnt = nbw_here > wk ? (nbw_here - wk + WK - 1) >> lwk : 0;
-    // block of step i; past the end, the wave's last real block; a wave with
-    // no block in the window refetches block wb0
-    auto blk = [&](int i) { return cnt > 0 ? wb0 + wk + WK * (i < cnt ? i : cnt - 1) : wb0; };
-    __syncthreads();  // earlier window fully consumed
-    // Stage the window.  Every batch but the last is full and waits for its
-    // own loads only; the last batch's loads (and the block scales) go out
-    // before the weight prefetch, so its wait does not cover the weights.
-    const int units = M * nbw_here;
-    const uint16_t* xw = X + 256 * wb0 + 8 * (threadIdx.x & 7);
-    const int per_batch = T >> 3;
-    PiecePos pos{0, (int)(threadIdx.x >> 3)};
-    while (pos.bw >= nbw_here) {
-      pos.bw -= nbw_here;
+  // Windows of nbw blocks (the last may be shorter).  nbw is a multiple of
+  // WK unless one window holds all of K, so in every full window each wave
+  // takes the same nbw / WK blocks: the waves walk one sequence of S steps,
+  // step s being block wk + WK s of window s / spw, and meet at the same
+  // window boundaries.  The weight ring runs on across the boundaries (the
+  // next window's first blocks are in flight while it is staged), and the
+  // first two staging batches of a window are loaded into registers one
+  // window ahead, so a boundary costs two barriers and the LDS stores.
+  const int per_batch = T >> 3;  // staging units per batch (eight threads each)
+  const int nwin = (nb + nbw - 1) / nbw;
+  const int spw = nbw >> lwk;               // steps per full window
+  const int S = (nb + WK - 1) >> lwk;       // steps of every wave
+  const int J = (nb - wk + WK - 1) >> lwk;  // steps with a block for this wave
+  auto gblk = [&](int s) { return wk + WK * (s < J ? s : J - 1); };
+
+  // Staging unit u of window w = (activation row u / nbw_w, window block
+  // u % nbw_w); thread t takes units t / 8 + per_batch b, b = 0, 1, ..., whose
+  // positions step by (dm, dbw) per batch without divisions.  Units past the
+  // window read row 0 and are not stored (or go to the trash area).
+  struct XBatch {
+    u32x4 v[4];
+    PiecePos pos;
+    bool ok;
+  };
+  XBatch xr[2];
+  auto x_step = [&](PiecePos& pos, int nbw_w, int dm, int dbw) {
+    pos.bw += dbw;
+    pos.m += dm;
+    if (pos.bw >= nbw_w) {
+      pos.bw -= nbw_w;
       ++pos.m;
     }
-    const int dm = per_batch / nbw_here;
-    const int dbw = per_batch - dm * nbw_here;
-    int q = 0;  // first unit of the batch
-    for (; q + per_batch < units; q += per_batch) {
-      u32x4 v[4];
-      piece_load(v, xw, pos, true, K);
-      piece_store(v, true, pos, smem, bias, trash, xstride, threadIdx.x & 7);
-      pos.bw += dbw;
-      pos.m += dm;
-      if (pos.bw >= nbw_here) {
-        pos.bw -= nbw_here;
-        ++pos.m;
-      }
+  };
+  auto x_issue = [&](int w) {  // loads of the first two batches of window w
+    const int nbw_w = min(nbw, nb - w * nbw);
+    const uint16_t* xw = X + 256 * w * nbw + 8 * (threadIdx.x & 7);
+    const int dm = per_batch / nbw_w;
+    const int dbw = per_batch - dm * nbw_w;
+    PiecePos pos{0, (int)(threadIdx.x >> 3)};
+    while (pos.bw >= nbw_w) {
+      pos.bw -= nbw_w;
+      ++pos.m;
     }
-    {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      xr[b].pos = pos;
+      xr[b].ok = pos.m < M;
+      piece_load(xr[b].v, xw, pos, xr[b].ok, K);
+      x_step(pos, nbw_w, dm, dbw);
+    }
+  };
+  auto x_store = [&](int w) {  // window w to LDS: the two batches held, then the rest
+    const int nbw_w = min(nbw, nb - w * nbw);
+    const uint16_t* xw = X + 256 * w * nbw + 8 * (threadIdx.x & 7);
+    const int dm = per_batch / nbw_w;
+    const int dbw = per_batch - dm * nbw_w;
+    // waves without a unit skip the store (their trash writes would all hit
+    // the same LDS banks)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+      if (__any(xr[b].ok)) piece_store(xr[b].v, xr[b].ok, xr[b].pos, smem, bias, trash, xstride, threadIdx.x & 7);
+    PiecePos pos = xr[1].pos;
+    x_step(pos, nbw_w, dm, dbw);
+    for (int q = 2 * per_batch; q < M * nbw_w; q += per_batch) {
       u32x4 v[4];
       const bool ok = pos.m < M;
       piece_load(v, xw, pos, ok, K);
-      // block scales: read in every window (straight-line), stored in the first
-      uint16_t sreg[kScaleRegs];
-      if constexpr (STAGE) {
-#pragma unroll
-        for (int r = 0; r < kScaleRegs; ++r) {
-          int e = threadIdx.x + r * T;
-          e = e < ns_all ? e : 0;
-          asm volatile("" : "+v"(e));  // keep the load in the window (not hoisted ahead of it)
-          sreg[r] = e < ns ? ssrc[e] : ssrc2[e - ns];
-        }
-      }
-      static_for<0, D>([&](auto dd) { load(decltype(dd)::value, blk(decltype(dd)::value)); });
-      // waves without a unit skip the store (their trash writes would all
-      // hit the same LDS banks)
       if (__any(ok)) piece_store(v, ok, pos, smem, bias, trash, xstride, threadIdx.x & 7);
-      if constexpr (STAGE) {
-        if (wb0 == 0) {
+      x_step(pos, nbw_w, dm, dbw);
+    }
+  };
+
+  // Window 0 and the block scales; the first ring loads go out after the
+  // window's and the scales' loads, so the wait for those does not cover them.
+  x_issue(0);
+  uint16_t sreg[kScaleRegs];
+  if constexpr (STAGE) {
 #pragma unroll
-          for (int r = 0; r < kScaleRegs; ++r) {
-            const int e = threadIdx.x + r * T;
-            // row of scale e: exact in fp32, since e < 2^14 keeps the rounding
-            // error far below the 0.5 / nb margin to the nearest integer
-            const int row = (int)(((float)e + 0.5f) * inv_nb);
-            if (e < ns_all) sc_lds[e + row] = h2f(sreg[r]);
-          }
-        }
-      }
+    for (int r = 0; r < kScaleRegs; ++r) {
+      int e = threadIdx.x + r * T;
+      e = e < ns_all ? e : 0;
+      asm volatile("" : "+v"(e));  // keep the load here (not hoisted ahead of the window's)
+      sreg[r] = e < ns ? ssrc[e] : ssrc2[e - ns];
     }
-    __syncthreads();
-    int i = 0;
-    for (; i + D < cnt; i += D) {
-      static_for<0, D>([&](auto dd) {
-        constexpr int d = decltype(dd)::value;
-        compute(d, blk(i + d), wk + WK * (i + d));
-        load(d, blk(i + d + D));
-      });
-    }
-    // last group: no loads past the wave's blocks
-    static_for<0, D>([&](auto dd) {
-      constexpr int d = decltype(dd)::value;
-      if (i + d < cnt) compute(d, blk(i + d), wk + WK * (i + d));
-    });
   }
+  static_for<0, D>([&](auto dd) { load(decltype(dd)::value, gblk(decltype(dd)::value)); });
+  x_store(0);
+  if constexpr (STAGE) {
+#pragma unroll
+    for (int r = 0; r < kScaleRegs; ++r) {
+      const int e = threadIdx.x + r * T;
+      // row of scale e: exact in fp32, since e < 2^14 keeps the rounding
+      // error far below the 0.5 / nb margin to the nearest integer
+      const int row = (int)(((float)e + 0.5f) * inv_nb);
+      if (e < ns_all) sc_lds[e + row] = h2f(sreg[r]);
+    }
+  }
+  __syncthreads();
+  if (nwin > 1) x_issue(1);
+
+  int w = 0;                                // window being computed
+  int next_b = nwin > 1 ? spw : S;          // first step of the next window
+  auto step = [&](auto dd, int s, auto with_load) {
+    constexpr int d = decltype(dd)::value;
+    if (s == next_b) {  // the same step in every wave
+      ++w;
+      __syncthreads();  // window w - 1 consumed
+      x_store(w);
+      __syncthreads();
+      if (w + 1 < nwin) x_issue(w + 1);
+      next_b = w + 1 < nwin ? next_b + spw : S;
+    }
+    if (s < J) compute(d, gblk(s), wk + WK * (s - w * spw));
+    if constexpr (decltype(with_load)::value) load(d, gblk(s + D));
+  };
+  int j = 0;
+  for (; j + D < S; j += D)
+    static_for<0, D>([&](auto dd) { step(dd, j + decltype(dd)::value, std::true_type{}); });
+  // last group: no loads past the steps
+  static_for<0, D>([&](auto dd) {
+    if (j + decltype(dd)::value < S) step(dd, j + decltype(dd)::value, std::false_type{});
+  });
 
   // Partial sums: every wave writes its 16 x 16 tile to LDS (reusing the
   // activation window); each tile element sums the WK waves of its row group.
@@ -432,16 +484,26 @@ hipError_t launch_skinny_rg(const GemmArgs& a, const void* qs2, const void* scal
   const int nb = K / 256;
   const int W = RG << lwk;
   if (lwk < 0 || W > 16) return hipErrorInvalidValue;
-  // activation window: as many blocks as fit the LDS budget with their sums
-  int nbw = (kXLdsMax - M * kXRowPad - kTrashBytes) / (M * 512 + kBiasBytes);
-  if (nbw > nb) nbw = nb;
-  if (nbw < 1) nbw = 1;
-  const int xbytes = M * (nbw * 512 + kXRowPad) + nbw * kBiasBytes + kTrashBytes;
-  int xregion = xbytes > W * 1024 ? xbytes : W * 1024;  // also holds the reduction
-  xregion = (xregion + 15) & ~15;
   const int64_t sbytes = scale_lds_bytes(RG, K);
   // staged: every thread holds at most kScaleRegs of the workgroup's scales
   const bool stage = sbytes <= kScaleLdsMax && int64_t{16} * RG * nb <= int64_t{kScaleRegs} * 64 * W;
+  // activation window: all of K when it fits the LDS left by the staged
+  // scales; else the fewest windows that fit, each a multiple of the 2^lwk
+  // waves of a row group (the kernel's waves then meet at the same window
+  // boundaries)
+  const int budget = kLdsLimit - (stage ? (int)sbytes : 0);
+  const int fit = (budget - M * kXRowPad - kTrashBytes) / (M * kBlkStride + kBiasBytes);
+  const int WK = 1 << lwk;
+  int nbw = nb;
+  if (fit < nb) {
+    const int nwin = (nb + fit - 1) / fit;
+    nbw = ((nb + nwin - 1) / nwin + WK - 1) / WK * WK;
+    if (nbw > fit) nbw = fit / WK * WK;
+    if (nbw < WK) return hipErrorInvalidValue;
+  }
+  const int xbytes = M * (nbw * kBlkStride + kXRowPad) + nbw * kBiasBytes + kTrashBytes;
+  int xregion = xbytes > W * 1024 ? xbytes : W * 1024;  // also holds the reduction
+  xregion = (xregion + 15) & ~15;
   const int lds = xregion + (stage ? (int)sbytes : 0);
   if (lds > kLdsLimit) return hipErrorInvalidValue;
   if (glu)
