@@ -107,6 +107,21 @@ def test_small_parity(fmt, path, M, N, K):
     check_close(Y, ref(X, T, s), f"{fmt}/{path}/{M}x{N}x{K}")
 
 
+# Skinny TQ2 shapes whose activations need several LDS windows: a short last
+# window in which some waves have no block (K = 5120, 9216, 6400), nb not a
+# multiple of the waves per row group, and seven windows (K = 28672).
+SKINNY_WINDOWS = [(16, 300, 5120), (16, 300, 28672), (9, 8192, 9216), (13, 1000, 6400)]
+
+
+@pytest.mark.parametrize("M,N,K", SKINNY_WINDOWS)
+def test_skinny_windows(M, N, K):
+    say(f"[windows] tq2 skinny M={M} N={N} K={K}")
+    T, s = iid_problem(N, K, 0.31, 5)
+    X = activations(M, K, 5)
+    Y = run("tq2", X, pack("tq2", T), s, "skinny").cpu().numpy()
+    check_close(Y, ref(X, T, s), f"windows {M}x{N}x{K}")
+
+
 def test_skinny_tq2_refuses_large_m():
     """The TQ2 skinny family serves M <= 16 only: a forced call past it returns
     TQ_ERR_UNSUPPORTED and writes nothing."""
@@ -532,13 +547,15 @@ def test_prefill_sizes(fmt, M, N):
 
 # ---- fused decode-step linears
 
-SWIGLU_SHAPES = [(1, 100, 256), (5, 300, 768), (16, 1000, 2048), (3, 4096, 8192)]
+SWIGLU_SHAPES = [(1, 100, 256), (5, 300, 768), (16, 1000, 2048), (3, 4096, 8192),
+                 (16, 1000, 6144)]
 
 
 @pytest.mark.parametrize("M,N,K", SWIGLU_SHAPES)
 def test_swiglu_parity(M, N, K):
     """Fused gate / up + SwiGLU against the fp64 oracle: ragged N, one to
-    several row groups per workgroup, K with 1..32 blocks."""
+    several row groups per workgroup, K with 1..32 blocks (the last in two
+    activation windows)."""
     from oracle import swiglu_ref
     say(f"[swiglu] M={M} N={N} K={K}")
     Tg, sg = iid_problem(N, K, 0.31, 41)
