@@ -27,10 +27,13 @@
 //    and scaled once (8 FMAs per lane per 16 rows);
 //  * activations, their block sums and the block scales are staged once per
 //    window of K (eight threads per 256 activations of a row, whose sum comes
-//    from v_dot2_f32_f16 and three DPP adds), the window's last loads issued
-//    before the first weight loads so that the wait for them does not wait for
-//    the weights; per-wave set-up is kept to shifts and masks (it is a large
-//    part of the time at one or two activation rows);
+//    from v_dot2_f32_f16 and three DPP adds; neighbouring threads swap pairs so
+//    that every LDS write is a dword), the first window's loads issued before
+//    the first weight loads so that the wait for them does not wait for the
+//    weights, later windows' loaded into registers a window ahead, with the
+//    weight ring running on across window boundaries; per-wave set-up is kept
+//    to shifts and masks (it is a large part of the time at one or two
+//    activation rows);
 //  * partial sums of the waves meet in LDS and one fp32 -> fp16 rounding writes
 //    Y.  No atomics: results are deterministic.
 
