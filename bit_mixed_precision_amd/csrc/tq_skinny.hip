@@ -210,8 +210,20 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   float* sc_lds = reinterpret_cast<float*>(smem + xregion);
 
   const int nrow = 16 * rgo + li < rows ? 16 * rgo + li : 0;  // row of this lane in the tile
-  const uint8_t* wrow = (up ? qs2 : qs) + (size_t)(n_base + nrow) * row_bytes + 16 * g;
   const uint16_t* srow = (up ? scales2 : scales) + (size_t)(n_base + nrow) * nb;
+  // Weights come in pairs of blocks, each 16-row pair as two loads of 8 rows
+  // x 128 contiguous bytes (whole cache lines; measured 15% faster to stream
+  // than 16 rows x 64 bytes).  Load A: rows 0..7 of the group, lane (n, g)
+  // taking piece g of block 0 for n < 8 and piece 4 + g (block 1) of row
+  // n - 8 for n >= 8; load B the same for rows 8..15 with the halves swapped.
+  // Block 0 in MFMA order is then A or B by lane, block 1 the other one
+  // rotated by 8 lanes (one DPP move).  Rows past N read row n_base.
+  const uint8_t* wq = up ? qs2 : qs;
+  const int ra = 16 * rgo + (li & 7), rb = ra + 8;
+  const int pa = li < 8 ? g : 4 + g, pb = li < 8 ? 4 + g : g;
+  const uint8_t* wrowa = wq + (size_t)(n_base + (ra < rows ? ra : 0)) * row_bytes + 16 * pa;
+  const uint8_t* wrowb = wq + (size_t)(n_base + (rb < rows ? rb : 0)) * row_bytes + 16 * pb;
+  const int npairs = (nb + 1) >> 1;
   const unsigned char* xa = smem + (li < M ? li : M - 1) * xstride + g * 128;
   const float* ba = bias + 4 * g;
 
@@ -228,21 +240,30 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   const float inv_nb = __builtin_amdgcn_rcpf((float)nb);  // within 1 ulp: ample for the row index
 
   float4v acc = {0.f, 0.f, 0.f, 0.f};
-  u32x4 wbuf[D];
-  uint16_t sbuf[D];
+  constexpr int P = D / 2;  // pairs of blocks in flight
+  u32x4 wa[P], wb[P];
+  uint16_t sbuf[P][2];
 
   // Weights are read once: non-temporal loads (measured 3-5% faster at
   // M <= 8 on both layer shapes than plain loads; the TQ1 kernel's 8-byte
-  // loads were slower with the hint, so it keeps plain ones).
-  auto load = [&](int d, int b) {
-    wbuf[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow + 64 * b));
-    if constexpr (!STAGE) sbuf[d] = srow[b];
+  // loads were slower with the hint, so it keeps plain ones).  Pair c holds
+  // blocks 2c and 2c + 1; with an odd block count the last pair's second half
+  // re-reads its first (never used).
+  auto load = [&](int d, int c) {
+    const int half2 = 2 * c + 1 < nb ? 64 : 0;
+    const int oa = 128 * c + (pa >= 4 ? half2 - 64 : 0);
+    const int ob = 128 * c + (pb >= 4 ? half2 - 64 : 0);
+    wa[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrowa + oa));
+    wb[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrowb + ob));
+    if constexpr (!STAGE) {
+      sbuf[d][0] = srow[2 * c];
+      sbuf[d][1] = srow[2 * c + 1 < nb ? 2 * c + 1 : 2 * c];
+    }
     __builtin_amdgcn_sched_barrier(0);  // keep the prefetch where it is
   };
-  auto compute = [&](int d, int b, int bw) {
-    const u32x4 w = wbuf[d];
+  auto compute = [&](const u32x4 w, uint16_t sb, int b, int bw) {
     const u32x4 w8 = shift8(w);
-    const float sc = STAGE ? sc_lds[sc_row + b] : h2f(sbuf[d]);
+    const float sc = STAGE ? sc_lds[sc_row + b] : h2f(sb);
     float4v c0 = *reinterpret_cast<const float4v*>(ba + 16 * bw);  // -2^-24 (row sums)
     float4v c1 = {0.f, 0.f, 0.f, 0.f};
     const unsigned char* xb = xa + bw * kBlkStride;
@@ -258,6 +279,17 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, __builtin_fmaf(c1[i], 0.0625f, c0[i]), acc[i]);
   };
+  auto compute_pair = [&](int d, int c, int bw0) {
+    u32x4 w0, w1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      w0[i] = li < 8 ? wa[d][i] : wb[d][i];
+      const uint32_t t = li < 8 ? wb[d][i] : wa[d][i];
+      w1[i] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)t, 0x128, 0xf, 0xf, false);  // row_ror:8
+    }
+    compute(w0, sbuf[d][0], 2 * c, bw0);
+    if (2 * c + 1 < nb) compute(w1, sbuf[d][1], 2 * c + 1, bw0 + 1);  // the same in every lane
+  };
 
   // Windows of nbw blocks (the last may be shorter).  nbw is a multiple of
   // WK unless one window holds all of K, so in every full window each wave
@@ -269,10 +301,10 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   // window ahead, so a boundary costs two barriers and the LDS stores.
   const int per_batch = T >> 3;  // staging units per batch (eight threads each)
   const int nwin = (nb + nbw - 1) / nbw;
-  const int spw = nbw >> lwk;               // steps per full window
-  const int S = (nb + WK - 1) >> lwk;       // steps of every wave
-  const int J = (nb - wk + WK - 1) >> lwk;  // steps with a block for this wave
-  auto gblk = [&](int s) { return wk + WK * (s < J ? s : J - 1); };
+  const int spw = (nbw >> 1) >> lwk;            // steps (pairs) per full window
+  const int S = (npairs + WK - 1) >> lwk;       // steps of every wave
+  const int J = (npairs - wk + WK - 1) >> lwk;  // steps with a pair for this wave
+  auto gpair = [&](int s) { return wk + WK * (s < J ? s : J - 1); };
 
   // Staging unit u of window w = (activation row u / nbw_w, window block
   // u % nbw_w); thread t takes units t / 8 + per_batch b, b = 0, 1, ..., whose
@@ -345,7 +377,7 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
       sreg[r] = e < ns ? ssrc[e] : ssrc2[e - ns];
     }
   }
-  static_for<0, D>([&](auto dd) { load(decltype(dd)::value, gblk(decltype(dd)::value)); });
+  static_for<0, P>([&](auto dd) { load(decltype(dd)::value, gpair(decltype(dd)::value)); });
   x_store(0);
   if constexpr (STAGE) {
 #pragma unroll
@@ -372,14 +404,14 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
       if (w + 1 < nwin) x_issue(w + 1);
       next_b = w + 1 < nwin ? next_b + spw : S;
     }
-    if (s < J) compute(d, gblk(s), wk + WK * (s - w * spw));
-    if constexpr (decltype(with_load)::value) load(d, gblk(s + D));
+    if (s < J) compute_pair(d, gpair(s), 2 * gpair(s) - w * nbw);
+    if constexpr (decltype(with_load)::value) load(d, gpair(s + P));
   };
   int j = 0;
-  for (; j + D < S; j += D)
-    static_for<0, D>([&](auto dd) { step(dd, j + decltype(dd)::value, std::true_type{}); });
+  for (; j + P < S; j += P)
+    static_for<0, P>([&](auto dd) { step(dd, j + decltype(dd)::value, std::true_type{}); });
   // last group: no loads past the steps
-  static_for<0, D>([&](auto dd) {
+  static_for<0, P>([&](auto dd) {
     if (j + decltype(dd)::value < S) step(dd, j + decltype(dd)::value, std::false_type{});
   });
 
@@ -449,16 +481,6 @@ int skinny_rows(int64_t N) { return pick_rows(N, device_cus()); }
 
 int skinny_depth() { return kDepth; }
 
-int skinny_lwk(int64_t N, int64_t K, int64_t M);
-
-int skinny_stage(int64_t N, int64_t K, int64_t M) {
-  const int64_t RG = skinny_rows(N);
-  const int64_t threads = 64 * (RG << skinny_lwk(N, K, M));
-  return scale_lds_bytes(RG, K) <= kScaleLdsMax && 16 * RG * (K / 256) <= kScaleRegs * threads
-             ? 1
-             : 0;
-}
-
 // Waves per row group: 2^lwk (a power of two, so the kernel's K slicing is
 // shifts and masks), at most 16 waves per workgroup.  For one or two
 // activation rows the per-wave set-up is a large part of the work, so waves
@@ -482,37 +504,60 @@ int skinny_lwk(int64_t N, int64_t K, int64_t M) {
   return lwk;
 }
 
-// Common launch: RG row groups in all (two matrices of RG / 2 each when
-// glu), 2^lwk waves per row group.
-hipError_t launch_skinny_rg(const GemmArgs& a, const void* qs2, const void* scales2, bool glu,
-                            hipStream_t stream, int RG, int lwk) {
-  const int M = (int)a.M, K = (int)a.K;
+// Launch plan for RG row groups and at most 2^lwk waves per row group:
+// every wave takes at least one pair of blocks, and when the activations
+// need windows, a window holds whole steps (a pair of blocks for each wave of
+// a row group, so that the waves meet at the same window boundaries); fewer
+// waves per row group when it cannot.  Block scales are staged in LDS when
+// every thread holds at most kScaleRegs (kScaleRegsGlu) of them.  The gate /
+// up kernel stages up to 32 KB (14 row groups at N = 28672: 29.5 KB;
+// measured 15-18% faster than loading each block's scales with its weights),
+// the plain one up to 24 KB (eight registers, loaded only as far as needed,
+// measured 3-6% slower for it at other shapes).
+struct SkinnyPlan {
+  int lwk, W, fit, unit;
+  bool stage;
+};
+
+bool plan_skinny(int M, int K, int RG, int lwk, bool glu, SkinnyPlan* p) {
   const int nb = K / 256;
-  const int W = RG << lwk;
-  if (lwk < 0 || W > 16) return hipErrorInvalidValue;
+  const int npairs = (nb + 1) / 2;
+  if (lwk < 0) return false;
+  while (lwk > 0 && (1 << lwk) > npairs) --lwk;
   const int64_t sbytes = scale_lds_bytes(RG, K);
-  // staged: every thread holds at most kScaleRegs (kScaleRegsGlu) of the
-  // workgroup's scales.  The gate / up kernel stages up to 32 KB (14 row
-  // groups at N = 28672: 29.5 KB; measured 15-18% faster than loading each
-  // block's scales with its weights), the plain one up to 24 KB (eight
-  // registers, loaded only as far as needed, measured 3-6% slower for it at
-  // other shapes).
   const int sregs = glu ? kScaleRegsGlu : kScaleRegs;
   const int64_t smax = glu ? kScaleLdsMaxGlu : kScaleLdsMax;
-  const bool stage = sbytes <= smax && int64_t{16} * RG * nb <= int64_t{sregs} * 64 * W;
+  for (;; --lwk) {
+    p->lwk = lwk;
+    p->W = RG << lwk;
+    if (p->W > 16) return false;
+    p->stage = sbytes <= smax && int64_t{16} * RG * nb <= int64_t{sregs} * 64 * p->W;
+    const int budget = kLdsLimit - (p->stage ? (int)sbytes : 0);
+    p->fit = (budget - M * kXRowPad - kTrashBytes) / (M * kBlkStride + kBiasBytes);
+    p->unit = 2 << lwk;
+    if (p->fit >= nb || p->fit >= p->unit || lwk == 0) return true;
+  }
+}
+
+// Common launch: RG row groups in all (two matrices of RG / 2 each when
+// glu), 2^lwk waves per row group at most.
+hipError_t launch_skinny_rg(const GemmArgs& a, const void* qs2, const void* scales2, bool glu,
+                            hipStream_t stream, int RG, int lwk_max) {
+  const int M = (int)a.M, K = (int)a.K;
+  const int nb = K / 256;
+  SkinnyPlan p;
+  if (!plan_skinny(M, K, RG, lwk_max, glu, &p)) return hipErrorInvalidValue;
+  const int lwk = p.lwk, W = p.W, fit = p.fit, unit = p.unit;
+  const bool stage = p.stage;
+  const int64_t sbytes = scale_lds_bytes(RG, K);
   // activation window: all of K when it fits the LDS left by the staged
-  // scales; else the fewest windows that fit, each a multiple of the 2^lwk
-  // waves of a row group (the kernel's waves then meet at the same window
-  // boundaries)
-  const int budget = kLdsLimit - (stage ? (int)sbytes : 0);
-  const int fit = (budget - M * kXRowPad - kTrashBytes) / (M * kBlkStride + kBiasBytes);
-  const int WK = 1 << lwk;
+  // scales; else the fewest windows that fit, each a multiple of a step
   int nbw = nb;
   if (fit < nb) {
     const int nwin = (nb + fit - 1) / fit;
-    nbw = ((nb + nwin - 1) / nwin + WK - 1) / WK * WK;
-    if (nbw > fit) nbw = fit / WK * WK;
-    if (nbw < WK) return hipErrorInvalidValue;
+    nbw = ((nb + nwin - 1) / nwin + unit - 1) / unit * unit;
+    if (nbw > fit) nbw = fit / unit * unit;
+    if (nbw < unit) return hipErrorInvalidValue;
   }
   const int xbytes = M * (nbw * kBlkStride + kXRowPad) + nbw * kBiasBytes + kTrashBytes;
   int xregion = xbytes > W * 1024 ? xbytes : W * 1024;  // also holds the reduction
@@ -524,6 +569,13 @@ hipError_t launch_skinny_rg(const GemmArgs& a, const void* qs2, const void* scal
                  : launch_tq2_skinny_s<false, true>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds);
   return stage ? launch_tq2_skinny_s<true, false>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds)
                : launch_tq2_skinny_s<false, false>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds);
+}
+
+int skinny_stage(int64_t N, int64_t K, int64_t M) {
+  SkinnyPlan p;
+  return plan_skinny((int)M, (int)K, skinny_rows(N), skinny_lwk(N, K, M), false, &p) && p.stage
+             ? 1
+             : 0;
 }
 
 hipError_t launch_tq2_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk) {
