@@ -76,7 +76,19 @@ struct Choice {
   int variant5 = -1;
 };
 
-constexpr int64_t kSkinnyMaxM = 16;
+constexpr int64_t kSkinnyMaxM = 16;     // one m tile of the TQ2 skinny kernel
+constexpr int64_t kSkinnyLimitM = 32;   // the TQ2 skinny kernel's limit (two m tiles)
+
+// TQ2 at 17..32 activation rows: the skinny kernel (every workgroup stages
+// all M x K activations, the weights stream once) beats the tiled one where
+// the weight rows per CU are many against the activation rows.  Measured
+// (K = 8192, us skinny / tiled): N = 28672 M = 17 28 / 40, M = 32 35 / 40;
+// N = 16384 M = 20 20.9 / 25.8, M = 32 24.4 / 25.7; N = 8192 M = 17
+// 13.4 / 17.7, M = 24 17.4 / 17.7, M = 32 20.3 / 17.7; N = 4096 M = 20
+// 17.0 / 15.1; K = 28672, N = 8192, M = 17 50.2 / 49.0.
+bool tq2_skinny_two_tiles(int64_t M, int64_t N, int64_t K) {
+  return M <= kSkinnyLimitM && K <= 16384 && N >= 384 * M;
+}
 
 // The kernel each (format, shape, path) runs.  Shapes are already validated.
 Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
@@ -84,7 +96,7 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
     if (tq1)
       path = M > kSkinnyMaxM && tq::tq1_prefers_tiled(M, N) ? TQ_PATH_TILED : TQ_PATH_SKINNY;
     else
-      path = M <= kSkinnyMaxM ? TQ_PATH_SKINNY : TQ_PATH_TILED;
+      path = M <= kSkinnyMaxM || tq2_skinny_two_tiles(M, N, K) ? TQ_PATH_SKINNY : TQ_PATH_TILED;
   }
   switch (path) {
     case TQ_PATH_SIMPLE:
@@ -94,9 +106,9 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
       if (tq1)
         return Choice{tq::launch_tq1_skinny, "tq1_skinny_kernel", tq::tq1_depth(),
                       tq::tq1_stage(N, K, M), tq::tq1_slices(M)};
-      if (M > kSkinnyMaxM) return Choice{nullptr, "", -1, -1};
-      return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_depth(),
-                    tq::skinny_stage(N, K, M)};
+      if (M > kSkinnyLimitM) return Choice{nullptr, "", -1, -1};
+      return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_depth(M),
+                    tq::skinny_stage(N, K, M), M > 16 ? 2 : 1};
     case TQ_PATH_TILED: {
       if (tq1) {
         const tq::Tq1TiledShape t = tq::tq1_tiled_shape(M, N);
@@ -195,8 +207,8 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
     snprintf(buf, sizeof buf, "%s<%d, %s, %d>", c.name, c.variant, c.variant2 ? "true" : "false",
              c.variant3);
   else if (c.variant2 >= 0 && c.launch == tq::launch_tq2_skinny)  // plain product: GLU = false
-    snprintf(buf, sizeof buf, "%s<%d, %s, false>", c.name, c.variant,
-             c.variant2 ? "true" : "false");
+    snprintf(buf, sizeof buf, "%s<%d, %s, false, %d>", c.name, c.variant,
+             c.variant2 ? "true" : "false", c.variant3);
   else if (c.variant5 >= 0)
     snprintf(buf, sizeof buf, "%s<%d, %d, %d, %d, %d>", c.name, c.variant, c.variant2,
              c.variant3, c.variant4, c.variant5);

@@ -35,7 +35,7 @@ hipError_t launch_tq1_simple(const GemmArgs& a, hipStream_t stream);
 // Skinny MFMA kernels for M <= 16; skinny_rows(N) is the number of 16-row
 // groups one workgroup owns (the template argument of the kernel).
 int skinny_rows(int64_t N);
-int skinny_depth();                      // register ring depth (template argument)
+int skinny_depth(int64_t M);             // register ring depth (template argument)
 int skinny_stage(int64_t N, int64_t K, int64_t M);  // 1 when block scales are staged in LDS
 hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream);
 // Fused decode-step gate / up product: a.qs / a.scales the gate matrix, Y =

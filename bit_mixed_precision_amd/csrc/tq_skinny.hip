@@ -73,12 +73,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 
 constexpr int kXRowPad = 16;          // bytes between LDS rows of Xt (bank spread)
 constexpr int kBlkStride = 512 + 32;  // bytes between the blocks of a row of Xt
-constexpr int kBiasBytes = 64;        // per block of the window: 16 fp32 row sums
+constexpr int kBiasBytes = 64;        // per block of the window and 16 rows: fp32 row sums
 constexpr int kScaleLdsMax = 24 * 1024;
 constexpr int kScaleLdsMaxGlu = 32 * 1024;  // the gate / up kernel's 2 x RG / 2 rows
 constexpr int kLdsLimit = 160 * 1024;
 constexpr int kScaleRegs = 4;         // block scales per thread loaded ahead
 constexpr int kScaleRegsGlu = 8;      // the same for the gate / up kernel
+constexpr int kWavesMt2 = 16;        // waves per workgroup with two m tiles
 constexpr int kTrashX = 512;          // trash area: one unit's activations, then its sum
 constexpr int kTrashBytes = kTrashX + 16;
 
@@ -138,7 +139,7 @@ __device__ __forceinline__ void piece_load(u32x4 (&v)[4], const uint16_t* __rest
 // odd one class 2 i + 1 at slots s - 1, s.
 __device__ __forceinline__ void piece_store(const u32x4 (&v)[4], bool ok, PiecePos p,
                                             unsigned char* xs, float* bias, unsigned char* trash,
-                                            int xstride, int s) {
+                                            int xstride, int s, int bstride) {
   const half2v quarter = {(_Float16)1.0f, (_Float16)0.25f};
   const half2v four = {(_Float16)1.0f, (_Float16)4.0f};
   float part = 0.f;
@@ -162,7 +163,7 @@ __device__ __forceinline__ void piece_store(const u32x4 (&v)[4], bool ok, PieceP
   part += dpp_f32<0xB1>(part);   // quad_perm [1, 0, 3, 2]
   part += dpp_f32<0x4E>(part);   // quad_perm [2, 3, 0, 1]
   part += dpp_f32<0x141>(part);  // row_half_mirror: the eight threads of the unit
-  float* bd = ok ? bias + p.bw * 16 + p.m : reinterpret_cast<float*>(trash + kTrashX);
+  float* bd = ok ? bias + p.bw * bstride + p.m : reinterpret_cast<float*>(trash + kTrashX);
   if (s == 0) *bd = part * -0x1p-24f;
 }
 
@@ -181,8 +182,8 @@ __device__ __forceinline__ void piece_store(const u32x4 (&v)[4], bool ok, PieceP
 // scales), the others the same rows of the up matrix (qs2, scales2), and the
 // output is silu(g) u of the two products (SwiGLU of the decode step), one
 // fp16 rounding.
-template <int D, bool STAGE, bool GLU>
-__global__ __launch_bounds__(1024) void tq2_skinny_kernel(
+template <int D, bool STAGE, bool GLU, int MT>
+__global__ __launch_bounds__(MT == 1 ? 1024 : 64 * kWavesMt2) void tq2_skinny_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ qs,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ qs2,
     const uint16_t* __restrict__ scales2, uint16_t* __restrict__ Y, int M, int N, int K, int RG,
@@ -205,8 +206,9 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   const int rows = min(16 * RGO, N - n_base);
   const int xstride = nbw * kBlkStride + kXRowPad;
   const size_t row_bytes = (size_t)(K >> 2);
+  constexpr int BS = 16 * MT;  // row sums per block
   float* bias = reinterpret_cast<float*>(smem + M * xstride);
-  unsigned char* trash = reinterpret_cast<unsigned char*>(bias + 16 * nbw);
+  unsigned char* trash = reinterpret_cast<unsigned char*>(bias + BS * nbw);
   float* sc_lds = reinterpret_cast<float*>(smem + xregion);
 
   const int nrow = 16 * rgo + li < rows ? 16 * rgo + li : 0;  // row of this lane in the tile
@@ -224,7 +226,12 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   const uint8_t* wrowa = wq + (size_t)(n_base + (ra < rows ? ra : 0)) * row_bytes + 16 * pa;
   const uint8_t* wrowb = wq + (size_t)(n_base + (rb < rows ? rb : 0)) * row_bytes + 16 * pb;
   const int npairs = (nb + 1) >> 1;
-  const unsigned char* xa = smem + (li < M ? li : M - 1) * xstride + g * 128;
+  // A operand rows of m tile t: activation rows 16 t + li (rows past M read
+  // row M - 1; their results are never written)
+  const unsigned char* xa[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+    xa[t] = smem + (16 * t + li < M ? 16 * t + li : M - 1) * xstride + g * 128;
   const float* ba = bias + 4 * g;
 
   // The workgroup's block scales (staged with the first window): ns of each
@@ -239,7 +246,9 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   const int sc_row = ((up ? rows : 0) + nrow) * (nb + 1);
   const float inv_nb = __builtin_amdgcn_rcpf((float)nb);  // within 1 ulp: ample for the row index
 
-  float4v acc = {0.f, 0.f, 0.f, 0.f};
+  float4v acc[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) acc[t] = float4v{0.f, 0.f, 0.f, 0.f};
   constexpr int P = D / 2;  // pairs of blocks in flight
   u32x4 wa[P], wb[P];
   uint16_t sbuf[P][2];
@@ -264,20 +273,24 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
   auto compute = [&](const u32x4 w, uint16_t sb, int b, int bw) {
     const u32x4 w8 = shift8(w);
     const float sc = STAGE ? sc_lds[sc_row + b] : h2f(sb);
-    float4v c0 = *reinterpret_cast<const float4v*>(ba + 16 * bw);  // -2^-24 (row sums)
-    float4v c1 = {0.f, 0.f, 0.f, 0.f};
-    const unsigned char* xb = xa + bw * kBlkStride;
-    auto A = [&](int c) { return *reinterpret_cast<const half8*>(xb + 16 * c); };
-    c0 = mfma16(A(0), tq2_class<0>(w, w8), c0);
-    c1 = mfma16(A(2), tq2_class<2>(w, w8), c1);
-    c0 = mfma16(A(1), tq2_class<1>(w, w8), c0);
-    c1 = mfma16(A(3), tq2_class<3>(w, w8), c1);
-    c0 = mfma16(A(4), tq2_class<4>(w, w8), c0);
-    c1 = mfma16(A(6), tq2_class<6>(w, w8), c1);
-    c0 = mfma16(A(5), tq2_class<5>(w, w8), c0);
-    c1 = mfma16(A(7), tq2_class<7>(w, w8), c1);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(sc, __builtin_fmaf(c1[i], 0.0625f, c0[i]), acc[i]);
+    for (int t = 0; t < MT; ++t) {
+      float4v c0 = *reinterpret_cast<const float4v*>(ba + BS * bw + 16 * t);  // -2^-24 (row sums)
+      float4v c1 = {0.f, 0.f, 0.f, 0.f};
+      const unsigned char* xb = xa[t] + bw * kBlkStride;
+      auto A = [&](int c) { return *reinterpret_cast<const half8*>(xb + 16 * c); };
+      c0 = mfma16(A(0), tq2_class<0>(w, w8), c0);
+      c1 = mfma16(A(2), tq2_class<2>(w, w8), c1);
+      c0 = mfma16(A(1), tq2_class<1>(w, w8), c0);
+      c1 = mfma16(A(3), tq2_class<3>(w, w8), c1);
+      c0 = mfma16(A(4), tq2_class<4>(w, w8), c0);
+      c1 = mfma16(A(6), tq2_class<6>(w, w8), c1);
+      c0 = mfma16(A(5), tq2_class<5>(w, w8), c0);
+      c1 = mfma16(A(7), tq2_class<7>(w, w8), c1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[t][i] = __builtin_fmaf(sc, __builtin_fmaf(c1[i], 0.0625f, c0[i]), acc[t][i]);
+    }
   };
   auto compute_pair = [&](int d, int c, int bw0) {
     u32x4 w0, w1;
@@ -351,14 +364,14 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
     // the same LDS banks)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
-      if (__any(xr[b].ok)) piece_store(xr[b].v, xr[b].ok, xr[b].pos, smem, bias, trash, xstride, threadIdx.x & 7);
+      if (__any(xr[b].ok)) piece_store(xr[b].v, xr[b].ok, xr[b].pos, smem, bias, trash, xstride, threadIdx.x & 7, BS);
     PiecePos pos = xr[1].pos;
     x_step(pos, nbw_w, dm, dbw);
     for (int q = 2 * per_batch; q < M * nbw_w; q += per_batch) {
       u32x4 v[4];
       const bool ok = pos.m < M;
       piece_load(v, xw, pos, ok, K);
-      if (__any(ok)) piece_store(v, ok, pos, smem, bias, trash, xstride, threadIdx.x & 7);
+      if (__any(ok)) piece_store(v, ok, pos, smem, bias, trash, xstride, threadIdx.x & 7, BS);
       x_step(pos, nbw_w, dm, dbw);
     }
   };
@@ -415,26 +428,30 @@ __global__ __launch_bounds__(1024) void tq2_skinny_kernel(
     if (j + decltype(dd)::value < S) step(dd, j + decltype(dd)::value, std::false_type{});
   });
 
-  // Partial sums: every wave writes its 16 x 16 tile to LDS (reusing the
-  // activation window); each tile element sums the WK waves of its row group.
+  // Partial sums: every wave writes its MT tiles of 16 x 16 to LDS (reusing
+  // the activation window); each tile element sums the WK waves of its row
+  // group.
   __syncthreads();
   float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[wave * 256 + i * 64 + lane] = acc[i];
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(wave * MT + t) * 256 + i * 64 + lane] = acc[t][i];
   __syncthreads();
-  for (int t = threadIdx.x; t < RGO * 256; t += T) {
-    const int r = t >> 8;
-    const int e = t & 255;
+  for (int q = threadIdx.x; q < RGO * MT * 256; q += T) {
+    const int r = q / (MT * 256);  // MT is 1 or 2: a shift
+    const int t = (q >> 8) & (MT - 1);
+    const int e = q & 255;
     const int l = e & 63;
-    const int m = 4 * (l >> 4) + (e >> 6);
+    const int m = 16 * t + 4 * (l >> 4) + (e >> 6);
     const int n = 16 * r + (l & 15);
     if (m < M && n < rows) {
       float sum = 0.f;
-      for (int k = 0; k < WK; ++k) sum += red[(r * WK + k) * 256 + e];
+      for (int k = 0; k < WK; ++k) sum += red[((r * WK + k) * MT + t) * 256 + e];
       sum *= 0x1p24f;
       if constexpr (GLU) {
         float u = 0.f;
-        for (int k = 0; k < WK; ++k) u += red[((RGO + r) * WK + k) * 256 + e];
+        for (int k = 0; k < WK; ++k) u += red[(((RGO + r) * WK + k) * MT + t) * 256 + e];
         sum = sum / (1.0f + expf(-sum)) * (u * 0x1p24f);  // silu(g) u
       }
       Y[(size_t)m * N + n_base + n] = f2h_bits(sum);
@@ -453,17 +470,19 @@ int pick_rows(int64_t N, int cus) {
 }
 
 constexpr int kDepth = 4;
+constexpr int kDepthMt2 = 2;  // (two m tiles: one pair in flight, within 128 VGPRs)
 
-template <bool STAGE, bool GLU>
+template <bool STAGE, bool GLU, int MT>
 hipError_t launch_tq2_skinny_s(const GemmArgs& a, const void* qs2, const void* scales2,
                                hipStream_t stream, int RG, int lwk, int nbw, int xregion, int lds) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = lds_limit_once(
-      reinterpret_cast<const void*>(tq2_skinny_kernel<kDepth, STAGE, GLU>), kLdsLimit, lds_set);
+      reinterpret_cast<const void*>(tq2_skinny_kernel<MT == 1 ? kDepth : kDepthMt2, STAGE, GLU, MT>),
+      kLdsLimit, lds_set);
   if (e != hipSuccess) return e;
   const int RGO = GLU ? RG / 2 : RG;
   const int64_t groups = (a.N + 16 * RGO - 1) / (16 * RGO);
-  hipLaunchKernelGGL((tq2_skinny_kernel<kDepth, STAGE, GLU>), dim3((unsigned)groups),
+  hipLaunchKernelGGL((tq2_skinny_kernel<MT == 1 ? kDepth : kDepthMt2, STAGE, GLU, MT>), dim3((unsigned)groups),
                      dim3(64 * (RG << lwk)), lds, stream, static_cast<const uint16_t*>(a.X),
                      static_cast<const uint8_t*>(a.qs), static_cast<const uint16_t*>(a.scales),
                      static_cast<const uint8_t*>(qs2), static_cast<const uint16_t*>(scales2),
@@ -479,7 +498,7 @@ int64_t scale_lds_bytes(int64_t RG, int64_t K) { return ((16 * RG * (K / 256 + 1
 
 int skinny_rows(int64_t N) { return pick_rows(N, device_cus()); }
 
-int skinny_depth() { return kDepth; }
+int skinny_depth(int64_t M) { return M > 16 ? kDepthMt2 : kDepth; }
 
 // Waves per row group: 2^lwk (a power of two, so the kernel's K slicing is
 // shifts and masks), at most 16 waves per workgroup.  For one or two
@@ -521,22 +540,40 @@ struct SkinnyPlan {
 
 bool plan_skinny(int M, int K, int RG, int lwk, bool glu, SkinnyPlan* p) {
   const int nb = K / 256;
+  const int mt = M > 16 ? 2 : 1;
   const int npairs = (nb + 1) / 2;
   if (lwk < 0) return false;
   while (lwk > 0 && (1 << lwk) > npairs) --lwk;
   const int64_t sbytes = scale_lds_bytes(RG, K);
   const int sregs = glu ? kScaleRegsGlu : kScaleRegs;
   const int64_t smax = glu ? kScaleLdsMaxGlu : kScaleLdsMax;
+  const int wmax = mt == 1 ? 16 : kWavesMt2;
+  while (lwk > 0 && (RG << lwk) > wmax) --lwk;
   for (;; --lwk) {
     p->lwk = lwk;
     p->W = RG << lwk;
-    if (p->W > 16) return false;
+    if (p->W > wmax) return false;
     p->stage = sbytes <= smax && int64_t{16} * RG * nb <= int64_t{sregs} * 64 * p->W;
     const int budget = kLdsLimit - (p->stage ? (int)sbytes : 0);
-    p->fit = (budget - M * kXRowPad - kTrashBytes) / (M * kBlkStride + kBiasBytes);
+    p->fit = (budget - M * kXRowPad - kTrashBytes) / (M * kBlkStride + mt * kBiasBytes);
     p->unit = 2 << lwk;
     if (p->fit >= nb || p->fit >= p->unit || lwk == 0) return true;
   }
+}
+
+template <int MT>
+hipError_t launch_skinny_mt(const GemmArgs& a, const void* qs2, const void* scales2, bool glu,
+                            bool stage, hipStream_t stream, int RG, int lwk, int nbw, int xregion,
+                            int lds) {
+  if constexpr (MT == 1) {  // the gate / up product serves M <= 16 only
+    if (glu)
+      return stage ? launch_tq2_skinny_s<true, true, MT>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds)
+                   : launch_tq2_skinny_s<false, true, MT>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds);
+  } else {
+    if (glu) return hipErrorInvalidValue;
+  }
+  return stage ? launch_tq2_skinny_s<true, false, MT>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds)
+               : launch_tq2_skinny_s<false, false, MT>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds);
 }
 
 // Common launch: RG row groups in all (two matrices of RG / 2 each when
@@ -545,6 +582,8 @@ hipError_t launch_skinny_rg(const GemmArgs& a, const void* qs2, const void* scal
                             hipStream_t stream, int RG, int lwk_max) {
   const int M = (int)a.M, K = (int)a.K;
   const int nb = K / 256;
+  if (M > 32) return hipErrorInvalidValue;
+  if (M > 16 && RG > kWavesMt2) RG = kWavesMt2;  // more, smaller workgroups (RG stays even)
   SkinnyPlan p;
   if (!plan_skinny(M, K, RG, lwk_max, glu, &p)) return hipErrorInvalidValue;
   const int lwk = p.lwk, W = p.W, fit = p.fit, unit = p.unit;
@@ -559,21 +598,21 @@ hipError_t launch_skinny_rg(const GemmArgs& a, const void* qs2, const void* scal
     if (nbw > fit) nbw = fit / unit * unit;
     if (nbw < unit) return hipErrorInvalidValue;
   }
-  const int xbytes = M * (nbw * kBlkStride + kXRowPad) + nbw * kBiasBytes + kTrashBytes;
-  int xregion = xbytes > W * 1024 ? xbytes : W * 1024;  // also holds the reduction
+  const int mt = M > 16 ? 2 : 1;
+  const int xbytes = M * (nbw * kBlkStride + kXRowPad) + nbw * mt * kBiasBytes + kTrashBytes;
+  int xregion = xbytes > W * 1024 * mt ? xbytes : W * 1024 * mt;  // also holds the reduction
   xregion = (xregion + 15) & ~15;
   const int lds = xregion + (stage ? (int)sbytes : 0);
   if (lds > kLdsLimit) return hipErrorInvalidValue;
-  if (glu)
-    return stage ? launch_tq2_skinny_s<true, true>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds)
-                 : launch_tq2_skinny_s<false, true>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds);
-  return stage ? launch_tq2_skinny_s<true, false>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds)
-               : launch_tq2_skinny_s<false, false>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds);
+  return mt == 1 ? launch_skinny_mt<1>(a, qs2, scales2, glu, stage, stream, RG, lwk, nbw, xregion, lds)
+                 : launch_skinny_mt<2>(a, qs2, scales2, glu, stage, stream, RG, lwk, nbw, xregion, lds);
 }
 
 int skinny_stage(int64_t N, int64_t K, int64_t M) {
   SkinnyPlan p;
-  return plan_skinny((int)M, (int)K, skinny_rows(N), skinny_lwk(N, K, M), false, &p) && p.stage
+  int RG = skinny_rows(N);
+  if (M > 16 && RG > kWavesMt2) RG = kWavesMt2;
+  return plan_skinny((int)M, (int)K, RG, skinny_lwk(N, K, M), false, &p) && p.stage
              ? 1
              : 0;
 }

@@ -23,7 +23,7 @@ torch = pytest.importorskip("torch")
 tq = pytest.importorskip("bit_mixed_precision_amd.binding")
 
 PATHS = {"simple": 3, "skinny": 1, "tiled": 2, "auto": 0}
-SKINNY_MAX_M = 16
+SKINNY_MAX_M = 32
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -90,7 +90,7 @@ SMALL = [(1, 1024, 1024), (2, 48, 512), (3, 100, 768), (4, 17, 256), (5, 64, 256
 
 
 # Every (format, family) at every small shape, except the TQ2 skinny family
-# past its M <= 16 limit (it refuses such calls: TQ_ERR_UNSUPPORTED, which
+# past its M <= 32 limit (it refuses such calls: TQ_ERR_UNSUPPORTED, which
 # test_skinny_tq2_refuses_large_m checks), so that a skip always means something.
 SMALL_CASES = [(fmt, path, M, N, K) for M, N, K in SMALL for fmt in ("tq2", "tq1")
                for path in ("simple", "skinny", "tiled", "auto")
@@ -109,8 +109,13 @@ def test_small_parity(fmt, path, M, N, K):
 
 # Skinny TQ2 shapes whose activations need several LDS windows: a short last
 # window in which some waves have no block (K = 5120, 9216, 6400), nb not a
-# multiple of the waves per row group, and seven windows (K = 28672).
-SKINNY_WINDOWS = [(16, 300, 5120), (16, 300, 28672), (9, 8192, 9216), (13, 1000, 6400)]
+# multiple of the waves per row group, and seven windows (K = 28672); with two
+# m tiles (M = 17 .. 32): windows of 8 blocks, a second m tile of one row
+# (M = 17), and more row groups than the 8 waves of such a workgroup
+# (N = 40000: 10 row groups per CU, run as 8).
+SKINNY_WINDOWS = [(16, 300, 5120), (16, 300, 28672), (9, 8192, 9216), (13, 1000, 6400),
+                  (32, 300, 5120), (17, 1000, 6400), (24, 2048, 8192), (32, 2048, 8192),
+                  (20, 40000, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", SKINNY_WINDOWS)
@@ -123,9 +128,9 @@ def test_skinny_windows(M, N, K):
 
 
 def test_skinny_tq2_refuses_large_m():
-    """The TQ2 skinny family serves M <= 16 only: a forced call past it returns
+    """The TQ2 skinny family serves M <= 32 only: a forced call past it returns
     TQ_ERR_UNSUPPORTED and writes nothing."""
-    M, N, K = 17, 64, 256
+    M, N, K = 33, 64, 256
     X = torch.zeros((M, K), dtype=torch.float16, device="cuda")
     q = torch.zeros((N, K // 4), dtype=torch.uint8, device="cuda")
     s = torch.ones((N, 1), dtype=torch.float16, device="cuda")
@@ -260,7 +265,7 @@ def test_exact_special_cases(fmt, path):
     (up to the stated offset rounding on the skinny paths)."""
     need(fmt, path)
     K = 512
-    for M in (1, 5, 16, 40):
+    for M in (1, 5, 16, 29, 40):
         if path == "skinny" and fmt == "tq2" and M > SKINNY_MAX_M:
             continue
         say(f"[exact] {fmt} {path} M={M}")
@@ -350,7 +355,7 @@ def test_latent_end_to_end():
         check_close(run("tq1", X, q1, s1, "auto").cpu().numpy(), R, f"latent tq1 {K}x{N}")
 
 
-FULL_M = [1, 2, 4, 8, 16, 32, 64, 128]
+FULL_M = [1, 2, 4, 8, 16, 20, 32, 64, 128]
 
 
 @pytest.mark.parametrize("N", [8192, 28672])
@@ -483,7 +488,7 @@ def test_outlier_next_to_subnormal_activations(fmt, path):
     K = 1536
     T, s = iid_problem(200, K, 0.31, 76)
     q = pack(fmt, T)
-    for M in ((5, 16) if fmt == "tq2" and path == "skinny" else (5, 16, 40)):
+    for M in ((5, 16, 32) if fmt == "tq2" and path == "skinny" else (5, 16, 40)):
         Xo, Xs = _wide_range_activations(M, K, 77 + M)
         say(f"[wide range] {fmt} {path} M={M}")
         Y = run(fmt, Xo, q, s, path).cpu().numpy()
