@@ -1,4 +1,4 @@
-// Skinny kernel for 2-bit weights (M <= 16): Y = X (s . T)^T with the weights
+// Skinny kernel for 2-bit weights (M <= 32): Y = X (s . T)^T with the weights
 // streamed once.
 //
 // The work follows the project page "Scaling Laws and Efficient Inference for
@@ -10,9 +10,10 @@
 //
 //  * a workgroup owns R groups of 16 weight rows and all of K; one workgroup
 //    per CU;
-//  * its waves take the 256-weight blocks round robin, so at any time they read
-//    neighbouring 64-byte pieces of the same rows; every lane streams 16-byte
-//    loads through a ring of register buffers;
+//  * its waves take pairs of 256-weight blocks round robin; a pair comes as
+//    two loads of 8 rows x 128 contiguous bytes (whole cache lines) through
+//    a ring of register buffers, and one DPP rotate per dword puts it in MFMA
+//    operand order;
 //  * one v_and_b32 per pair of weights is the whole decode: masking a 2-bit
 //    field that sits at mantissa bits 2p..2p+1 of an fp16 with a zero exponent
 //    leaves the exact subnormal d' 4^p 2^-24, which the MFMA multiplies exactly
@@ -22,9 +23,9 @@
 //    scaled by 1 or 1/4 only (exact above the fp16 subnormal range);
 //  * the shift d = d' - 1 costs no per-weight work: the sum of the block's
 //    activations, taken in fp32 while staging them, seeds the first chain;
-//  * the multiply-accumulate runs on v_mfma_f32_16x16x32_f16 with the M <= 16
-//    activation rows as the A operand; per block the two chains are combined
-//    and scaled once (8 FMAs per lane per 16 rows);
+//  * the multiply-accumulate runs on v_mfma_f32_16x16x32_f16 with one or two
+//    tiles of 16 activation rows as the A operand; per block the two chains
+//    are combined and scaled once (8 FMAs per lane per 16 rows);
 //  * activations, their block sums and the block scales are staged once per
 //    window of K (eight threads per 256 activations of a row, whose sum comes
 //    from v_dot2_f32_f16 and three DPP adds; neighbouring threads swap pairs so
@@ -169,11 +170,12 @@ __device__ __forceinline__ void piece_store(const u32x4 (&v)[4], bool ok, PieceP
 
 // A workgroup owns RG groups of 16 weight rows and all of K.  Its RG * WK
 // waves (WK = 2^lwk) are light: wave w works on row group w / WK and on the
-// blocks b = w % WK + WK * i of K, so several waves per SIMD interleave decode,
-// MFMA and memory waits.  Each wave keeps a ring of D register buffers of weights
-// in flight; the loop body is straight-line except for the last group of
-// steps, which issues no loads, so the compiler's wait before each decode
-// covers exactly the oldest buffer.  STAGE: the block scales of the
+// pairs of blocks c = w % WK + WK * i of K, so several waves per SIMD
+// interleave decode, MFMA and memory waits.  MT tiles of 16 activation rows
+// share every decoded weight operand.  Each wave keeps D / 2 pairs of blocks
+// in flight in a register ring; the loop body is straight-line except for
+// the last group of steps, which issues no loads, so the compiler's wait
+// before each decode covers exactly the oldest pair.  STAGE: the block scales of the
 // workgroup's rows are copied to LDS as fp32 (else each block's scale comes
 // with its weights).  Rows past N and activation rows past M read valid dummy
 // data whose results are never written (MFMA rows and columns do not mix).
@@ -305,9 +307,9 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 64 * kWavesMt2) void tq2_skinny_ke
   };
 
   // Windows of nbw blocks (the last may be shorter).  nbw is a multiple of
-  // WK unless one window holds all of K, so in every full window each wave
-  // takes the same nbw / WK blocks: the waves walk one sequence of S steps,
-  // step s being block wk + WK s of window s / spw, and meet at the same
+  // 2 WK unless one window holds all of K, so in every full window each wave
+  // takes the same nbw / (2 WK) pairs: the waves walk one sequence of S steps,
+  // step s being pair wk + WK s, in window s / spw, and meet at the same
   // window boundaries.  The weight ring runs on across the boundaries (the
   // next window's first blocks are in flight while it is staged), and the
   // first two staging batches of a window are loaded into registers one
