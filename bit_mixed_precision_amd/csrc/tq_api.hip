@@ -108,7 +108,8 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
                       tq::tq1_stage(N, K, M), tq::tq1_slices(M)};
       if (M > kSkinnyLimitM) return Choice{nullptr, "", -1, -1};
       return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_depth(M),
-                    tq::skinny_stage(N, K, M), M > 16 ? 2 : 1};
+                    tq::skinny_stage(N, K, M), M > 16 ? 2 : 1,
+                    tq::skinny_ring_first(M, K) ? 1 : 0};
     case TQ_PATH_TILED: {
       if (tq1) {
         const tq::Tq1TiledShape t = tq::tq1_tiled_shape(M, N);
@@ -207,8 +208,8 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
     snprintf(buf, sizeof buf, "%s<%d, %s, %d>", c.name, c.variant, c.variant2 ? "true" : "false",
              c.variant3);
   else if (c.variant2 >= 0 && c.launch == tq::launch_tq2_skinny)  // plain product: GLU = false
-    snprintf(buf, sizeof buf, "%s<%d, %s, false, %d>", c.name, c.variant,
-             c.variant2 ? "true" : "false", c.variant3);
+    snprintf(buf, sizeof buf, "%s<%d, %s, false, %d, %s>", c.name, c.variant,
+             c.variant2 ? "true" : "false", c.variant3, c.variant4 ? "true" : "false");
   else if (c.variant5 >= 0)
     snprintf(buf, sizeof buf, "%s<%d, %d, %d, %d, %d>", c.name, c.variant, c.variant2,
              c.variant3, c.variant4, c.variant5);

@@ -36,6 +36,7 @@ hipError_t launch_tq1_simple(const GemmArgs& a, hipStream_t stream);
 // groups one workgroup owns (the template argument of the kernel).
 int skinny_rows(int64_t N);
 int skinny_depth(int64_t M);             // register ring depth (template argument)
+bool skinny_ring_first(int64_t M, int64_t K);  // ring loads before the activation wait
 int skinny_stage(int64_t N, int64_t K, int64_t M);  // 1 when block scales are staged in LDS
 hipError_t launch_tq2_skinny(const GemmArgs& a, hipStream_t stream);
 // Fused decode-step gate / up product: a.qs / a.scales the gate matrix, Y =

@@ -180,11 +180,15 @@ __device__ __forceinline__ void piece_store(const u32x4 (&v)[4], bool ok, PieceP
 // with its weights).  Rows past N and activation rows past M read valid dummy
 // data whose results are never written (MFMA rows and columns do not mix).
 //
+// RF: the first ring loads go out before the wait for the first window's
+// activations (else after their LDS stores, so that they do not compete with
+// a large activation copy).
+//
 // GLU: the workgroup's first RG / 2 row groups read the gate matrix (qs,
 // scales), the others the same rows of the up matrix (qs2, scales2), and the
 // output is silu(g) u of the two products (SwiGLU of the decode step), one
 // fp16 rounding.
-template <int D, bool STAGE, bool GLU, int MT>
+template <int D, bool STAGE, bool GLU, int MT, bool RF>
 __global__ __launch_bounds__(MT == 1 ? 1024 : 64 * kWavesMt2) void tq2_skinny_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ qs,
     const uint16_t* __restrict__ scales, const uint8_t* __restrict__ qs2,
@@ -392,8 +396,12 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 64 * kWavesMt2) void tq2_skinny_ke
       sreg[r] = e < ns ? ssrc[e] : ssrc2[e - ns];
     }
   }
-  static_for<0, P>([&](auto dd) { load(decltype(dd)::value, gpair(decltype(dd)::value)); });
+  auto ring_start = [&] {
+    static_for<0, P>([&](auto dd) { load(decltype(dd)::value, gpair(decltype(dd)::value)); });
+  };
+  if constexpr (RF) ring_start();
   x_store(0);
+  if constexpr (!RF) ring_start();
   if constexpr (STAGE) {
 #pragma unroll
     for (int r = 0; r < SR; ++r) {
@@ -474,17 +482,17 @@ int pick_rows(int64_t N, int cus) {
 constexpr int kDepth = 4;
 constexpr int kDepthMt2 = 2;  // (two m tiles: one pair in flight, within 128 VGPRs)
 
-template <bool STAGE, bool GLU, int MT>
+template <bool STAGE, bool GLU, int MT, bool RF>
 hipError_t launch_tq2_skinny_s(const GemmArgs& a, const void* qs2, const void* scales2,
                                hipStream_t stream, int RG, int lwk, int nbw, int xregion, int lds) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = lds_limit_once(
-      reinterpret_cast<const void*>(tq2_skinny_kernel<MT == 1 ? kDepth : kDepthMt2, STAGE, GLU, MT>),
+      reinterpret_cast<const void*>(tq2_skinny_kernel<MT == 1 ? kDepth : kDepthMt2, STAGE, GLU, MT, RF>),
       kLdsLimit, lds_set);
   if (e != hipSuccess) return e;
   const int RGO = GLU ? RG / 2 : RG;
   const int64_t groups = (a.N + 16 * RGO - 1) / (16 * RGO);
-  hipLaunchKernelGGL((tq2_skinny_kernel<MT == 1 ? kDepth : kDepthMt2, STAGE, GLU, MT>), dim3((unsigned)groups),
+  hipLaunchKernelGGL((tq2_skinny_kernel<MT == 1 ? kDepth : kDepthMt2, STAGE, GLU, MT, RF>), dim3((unsigned)groups),
                      dim3(64 * (RG << lwk)), lds, stream, static_cast<const uint16_t*>(a.X),
                      static_cast<const uint8_t*>(a.qs), static_cast<const uint16_t*>(a.scales),
                      static_cast<const uint8_t*>(qs2), static_cast<const uint16_t*>(scales2),
@@ -501,6 +509,15 @@ int64_t scale_lds_bytes(int64_t RG, int64_t K) { return ((16 * RG * (K / 256 + 1
 int skinny_rows(int64_t N) { return pick_rows(N, device_cus()); }
 
 int skinny_depth(int64_t M) { return M > 16 ? kDepthMt2 : kDepth; }
+
+// The first ring loads go out before the first window's activation wait when
+// the copy is small (under 48 KB of activations), else after its LDS stores:
+// a large copy then reaches LDS without the weight stream in its way.
+// Measured (us, ring first / after): M = 8, N = K = 8192 9.0 / 7.8; M = 16,
+// N = 28672 21.2 / 20.7; K = 28672, N = 8192, M = 1 16.2 / 15.6; the gate /
+// up product at M = 16 35.2 / 34.2; and the other way round for small copies:
+// 3072 x 3072 4.07 / 4.29, K = 8192 with N = 3072 5.42 / 5.61 (M = 1).
+bool skinny_ring_first(int64_t M, int64_t K) { return M * K < 24576; }
 
 // Waves per row group: 2^lwk (a power of two, so the kernel's K slicing is
 // shifts and masks), at most 16 waves per workgroup.  For one or two
@@ -563,19 +580,19 @@ bool plan_skinny(int M, int K, int RG, int lwk, bool glu, SkinnyPlan* p) {
   }
 }
 
-template <int MT>
+template <int MT, bool RF>
 hipError_t launch_skinny_mt(const GemmArgs& a, const void* qs2, const void* scales2, bool glu,
                             bool stage, hipStream_t stream, int RG, int lwk, int nbw, int xregion,
                             int lds) {
   if constexpr (MT == 1) {  // the gate / up product serves M <= 16 only
     if (glu)
-      return stage ? launch_tq2_skinny_s<true, true, MT>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds)
-                   : launch_tq2_skinny_s<false, true, MT>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds);
+      return stage ? launch_tq2_skinny_s<true, true, MT, RF>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds)
+                   : launch_tq2_skinny_s<false, true, MT, RF>(a, qs2, scales2, stream, RG, lwk, nbw, xregion, lds);
   } else {
     if (glu) return hipErrorInvalidValue;
   }
-  return stage ? launch_tq2_skinny_s<true, false, MT>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds)
-               : launch_tq2_skinny_s<false, false, MT>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds);
+  return stage ? launch_tq2_skinny_s<true, false, MT, RF>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds)
+               : launch_tq2_skinny_s<false, false, MT, RF>(a, a.qs, a.scales, stream, RG, lwk, nbw, xregion, lds);
 }
 
 // Common launch: RG row groups in all (two matrices of RG / 2 each when
@@ -606,8 +623,12 @@ hipError_t launch_skinny_rg(const GemmArgs& a, const void* qs2, const void* scal
   xregion = (xregion + 15) & ~15;
   const int lds = xregion + (stage ? (int)sbytes : 0);
   if (lds > kLdsLimit) return hipErrorInvalidValue;
-  return mt == 1 ? launch_skinny_mt<1>(a, qs2, scales2, glu, stage, stream, RG, lwk, nbw, xregion, lds)
-                 : launch_skinny_mt<2>(a, qs2, scales2, glu, stage, stream, RG, lwk, nbw, xregion, lds);
+  const bool rf = skinny_ring_first(M, K);
+  if (mt == 1)
+    return rf ? launch_skinny_mt<1, true>(a, qs2, scales2, glu, stage, stream, RG, lwk, nbw, xregion, lds)
+              : launch_skinny_mt<1, false>(a, qs2, scales2, glu, stage, stream, RG, lwk, nbw, xregion, lds);
+  return rf ? launch_skinny_mt<2, true>(a, qs2, scales2, glu, stage, stream, RG, lwk, nbw, xregion, lds)
+            : launch_skinny_mt<2, false>(a, qs2, scales2, glu, stage, stream, RG, lwk, nbw, xregion, lds);
 }
 
 int skinny_stage(int64_t N, int64_t K, int64_t M) {
