@@ -105,7 +105,8 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
     case TQ_PATH_SKINNY:
       if (tq1)
         return Choice{tq::launch_tq1_skinny, "tq1_skinny_kernel", tq::tq1_depth(),
-                      tq::tq1_stage(N, K, M), tq::tq1_slices(M)};
+                      tq::tq1_stage(N, K, M), tq::tq1_slices(M),
+                      tq::tq1_ring_first(N, K, M) ? 1 : 0};
       if (M > kSkinnyLimitM) return Choice{nullptr, "", -1, -1};
       return Choice{tq::launch_tq2_skinny, "tq2_skinny_kernel", tq::skinny_depth(M),
                     tq::skinny_stage(N, K, M), M > 16 ? 2 : 1,
@@ -205,8 +206,8 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
   if (!c.launch) return TQ_ERR_UNSUPPORTED;
   char buf[160];
   if (c.launch == tq::launch_tq1_skinny)
-    snprintf(buf, sizeof buf, "%s<%d, %s, %d>", c.name, c.variant, c.variant2 ? "true" : "false",
-             c.variant3);
+    snprintf(buf, sizeof buf, "%s<%d, %s, %d, %s>", c.name, c.variant,
+             c.variant2 ? "true" : "false", c.variant3, c.variant4 ? "true" : "false");
   else if (c.variant2 >= 0 && c.launch == tq::launch_tq2_skinny)  // plain product: GLU = false
     snprintf(buf, sizeof buf, "%s<%d, %s, false, %d, %s>", c.name, c.variant,
              c.variant2 ? "true" : "false", c.variant3, c.variant4 ? "true" : "false");

@@ -59,6 +59,8 @@ hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream);
 int tq1_depth();
 int tq1_stage(int64_t N, int64_t K, int64_t M);
 int tq1_slices(int64_t M);  // 16-row activation slices per workgroup (template argument)
+int tq1_window_spans(int64_t M, int64_t K, int W);  // spans per activation window
+bool tq1_ring_first(int64_t N, int64_t K, int64_t M);  // ring loads before the activation store
 
 // Tiled MFMA kernels for M > 16: a workgroup of 4 waves (ng weight-row
 // groups x kg k-groups) owns 16 mt activation rows x 16 nr ng weight rows.

@@ -162,7 +162,10 @@ __device__ __forceinline__ void tq1_store_unit(const Tq1Unit& un, unsigned char*
   }
 }
 
-template <int D, bool STAGE, int MS>
+// RF: each window's first ring loads go out before the window's activations
+// are stored (else after: with one window, whose activations were loaded at
+// the start, the weight stream then does not delay their copy).
+template <int D, bool STAGE, int MS, bool RF>
 __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ qs, int ldq,
     const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int M, int N, int K, int RG,
@@ -298,11 +301,15 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
     const int nuw_here = min(nuw, nu - u0);
     const int cnt = nuw_here > wk ? (nuw_here - wk + WK - 1) >> lwk : 0;
     auto span = [&](int i) { return cnt > 0 ? u0 + wk + WK * (i < cnt ? i : cnt - 1) : u0; };
-    sfor1<0, D>([&](auto dd) { load(decltype(dd)::value, span(decltype(dd)::value)); });
+    auto ring_start = [&] {
+      sfor1<0, D>([&](auto dd) { load(decltype(dd)::value, span(decltype(dd)::value)); });
+    };
+    if constexpr (RF) ring_start();
     __syncthreads();  // the previous window is consumed
     // waves without a unit skip the store (their trash writes would all hit
     // the same LDS banks)
     if (__any(un.ok)) tq1_store_unit(un, smem, sums, trash, u0, q & 3, xstride, K);
+    if constexpr (!RF) ring_start();
     if constexpr (STAGE) {
       if (u0 == 0) {
 #pragma unroll
@@ -371,14 +378,14 @@ __global__ __launch_bounds__(1024) void tq1_skinny_kernel(
 
 constexpr int kDepth1 = 3;
 
-template <bool STAGE, int MS>
+template <bool STAGE, int MS, bool RF>
 hipError_t launch_tq1_s(const GemmArgs& a, hipStream_t stream, dim3 grid, int W, int lds, int RG,
                         int lwk, int nuw, int xregion) {
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = lds_limit_once(
-      reinterpret_cast<const void*>(tq1_skinny_kernel<kDepth1, STAGE, MS>), kLdsMax, lds_set);
+      reinterpret_cast<const void*>(tq1_skinny_kernel<kDepth1, STAGE, MS, RF>), kLdsMax, lds_set);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((tq1_skinny_kernel<kDepth1, STAGE, MS>), grid, dim3(64 * W), lds, stream,
+  hipLaunchKernelGGL((tq1_skinny_kernel<kDepth1, STAGE, MS, RF>), grid, dim3(64 * W), lds, stream,
                      static_cast<const uint16_t*>(a.X), static_cast<const uint8_t*>(a.qs),
                      (int)a.ldq, static_cast<const uint16_t*>(a.scales),
                      static_cast<uint16_t*>(a.Y), (int)a.M, (int)a.N, (int)a.K, RG, lwk, nuw,
@@ -386,11 +393,11 @@ hipError_t launch_tq1_s(const GemmArgs& a, hipStream_t stream, dim3 grid, int W,
   return hipGetLastError();
 }
 
-template <bool STAGE>
+template <bool STAGE, bool RF>
 hipError_t launch_tq1_ms(int ms, const GemmArgs& a, hipStream_t stream, dim3 grid, int W, int lds,
                          int RG, int lwk, int nuw, int xregion) {
-  if (ms == 2) return launch_tq1_s<STAGE, 2>(a, stream, grid, W, lds, RG, lwk, nuw, xregion);
-  return launch_tq1_s<STAGE, 1>(a, stream, grid, W, lds, RG, lwk, nuw, xregion);
+  if (ms == 2) return launch_tq1_s<STAGE, 2, RF>(a, stream, grid, W, lds, RG, lwk, nuw, xregion);
+  return launch_tq1_s<STAGE, 1, RF>(a, stream, grid, W, lds, RG, lwk, nuw, xregion);
 }
 
 // Staged scales: 16 RG rows of K / 256 floats, rows padded by one float.
@@ -399,6 +406,19 @@ int64_t tq1_scale_bytes(int64_t RG, int64_t K) { return ((16 * RG * (K / 256 + 1
 }  // namespace
 
 int tq1_depth() { return kDepth1; }
+
+// Spans of 160 weights per activation window: as many as fit the LDS and
+// one staging unit per thread (W waves), at most all of K.
+int tq1_window_spans(int64_t M, int64_t K, int W) {
+  const int64_t nu = (((K + 4) / 5) + 31) / 32;
+  const int64_t ms = tq1_slices(M);
+  const int64_t mrows = M < 16 * ms ? M : 16 * ms;
+  int64_t nuw = (kXLds - mrows * kPad - kTrash) / (mrows * kSpanBytes + kSumBytes);
+  if (nuw > nu) nuw = nu;
+  if (nuw > 64 * W / (4 * mrows)) nuw = 64 * W / (4 * mrows);  // one staging unit per thread
+  return (int)nuw;
+}
+
 
 int tq1_slices(int64_t M) { return M <= 16 ? 1 : 2; }
 
@@ -424,10 +444,24 @@ int tq1_lwk(int64_t N, int64_t K, int64_t M) {
   return lwk;
 }
 
+// The ring goes first only with several activation windows and fewer than 12
+// waves: with one window (activations loaded at the start) the weight stream
+// after the activation store measured faster (M = 1, N = 8192: 10.4 -> 10.0
+// us; 3072 x 3072 6.25 -> 5.68), and so it did with 14-16 waves over several
+// windows (M = 16, N = 28672: 38.7 -> 37.4; K = 28672, N = 8192, M = 1: 26.5
+// -> 25.5), but with 8 waves over 7 windows each window's ring restart then
+// waits for the barrier (M = 16, N = 8192: 21.5 -> 22.6).
+bool tq1_ring_first_w(int64_t K, int64_t M, int W) {
+  const int64_t nu = (((K + 4) / 5) + 31) / 32;
+  return tq1_window_spans(M, K, W) < nu && W < 12;
+}
+
+bool tq1_ring_first(int64_t N, int64_t K, int64_t M) {
+  return tq1_ring_first_w(K, M, skinny_rows(N) << tq1_lwk(N, K, M));
+}
+
 hipError_t launch_tq1_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk) {
   const int M = (int)a.M, K = (int)a.K;
-  const int groups = (K + 4) / 5;
-  const int nu = (groups + 31) / 32;
   const int RG = skinny_rows(a.N);
   const int W = RG << lwk;
   if (lwk < 0 || W > 16) return hipErrorInvalidValue;
@@ -437,9 +471,7 @@ hipError_t launch_tq1_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk)
   // and the 1024-thread workgroup runs out of registers).
   const int ms = tq1_slices(M);
   const int mrows = M < 16 * ms ? M : 16 * ms;
-  int nuw = (kXLds - mrows * kPad - kTrash) / (mrows * kSpanBytes + kSumBytes);
-  if (nuw > nu) nuw = nu;
-  if (nuw > 64 * W / (4 * mrows)) nuw = 64 * W / (4 * mrows);  // one staging unit per thread
+  const int nuw = tq1_window_spans(M, K, W);
   if (nuw < 1) return hipErrorInvalidValue;
   const int xbytes = mrows * (nuw * kSpanBytes + kPad) + nuw * kSumBytes + kTrash;
   const int rbytes = ms * W * 1024;  // the partial sums reuse the window
@@ -451,8 +483,11 @@ hipError_t launch_tq1_skinny_lwk(const GemmArgs& a, hipStream_t stream, int lwk)
   const int lds = xregion + (stage ? (int)sbytes : 0);
   if (lds > kLdsMax) return hipErrorInvalidValue;
   dim3 grid((unsigned)((a.N + 16 * RG - 1) / (16 * RG)), (unsigned)((a.M + 16 * ms - 1) / (16 * ms)));
-  return stage ? launch_tq1_ms<true>(ms, a, stream, grid, W, lds, RG, lwk, nuw, xregion)
-               : launch_tq1_ms<false>(ms, a, stream, grid, W, lds, RG, lwk, nuw, xregion);
+  if (!tq1_ring_first_w(K, M, W))
+    return stage ? launch_tq1_ms<true, false>(ms, a, stream, grid, W, lds, RG, lwk, nuw, xregion)
+                 : launch_tq1_ms<false, false>(ms, a, stream, grid, W, lds, RG, lwk, nuw, xregion);
+  return stage ? launch_tq1_ms<true, true>(ms, a, stream, grid, W, lds, RG, lwk, nuw, xregion)
+               : launch_tq1_ms<false, true>(ms, a, stream, grid, W, lds, RG, lwk, nuw, xregion);
 }
 
 hipError_t launch_tq1_skinny(const GemmArgs& a, hipStream_t stream) {
