@@ -102,7 +102,8 @@ struct TileGeom {
   static constexpr RingPlan kPlan = ring_plan(kStage, kWRound, kBudget);
   static constexpr int XS = kPlan.xs;
   static constexpr int WD = kPlan.wd;
-  static_assert(XS <= 4 * WD - 1, "weights must arrive before the stage that reads them");
+  static constexpr int WCH = w_issue_ch(WD);  // stage of a round that issues weights
+  static_assert(XS <= 4 * WD - WCH, "weights must arrive before the stage that reads them");
   static_assert(XS <= 6, "round 0 is the only round whose wait window reaches the prologue");
   static constexpr int kRing = XS * kStage;
   static constexpr int RG8 = BM / 8;          // 8-row DMA groups per chunk
@@ -279,14 +280,14 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
       const int s = 4 * rd + ch;
       // Stage s's DMA came XS - 1 iterations ago and is the last DMA of its
       // iteration; younger are the activation DMAs of the XS - 2 iterations
-      // after it and the weight/scale DMA of those among them with ch = 1
+      // after it and the weight/scale DMA of those among them with ch = WCH
       // (issued first in its iteration).  Round rd + 1's weights, read at
-      // ch = 3, are older than stage 4 rd + 3's DMA (XS <= 4 WD - 1).
+      // ch = 3, are older than stage 4 rd + 3's DMA (XS <= 4 WD - WCH).
       mem_clobber();
       if (rd == 0)
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_younger(G::XS, G::kPer, kWIssue, ch, true)));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_younger(G::XS, G::kPer, kWIssue, ch, true, G::WCH)));
       else
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_younger(G::XS, G::kPer, kWIssue, ch, false)));
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(vm_younger(G::XS, G::kPer, kWIssue, ch, false, G::WCH)));
       __builtin_amdgcn_s_barrier();
       mem_clobber();
       const unsigned char* base = smem + (uint32_t)(s % G::XS) * G::kStage + wk * G::kChunk;
@@ -299,8 +300,8 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
       if constexpr (ch == 3) read_w(rd + 1, wnx, s2n);  // stale refill past the end
       // all LDS reads of the stage are in flight before any of them is used
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (ch == 1) issue_w(rd + G::WD);  // its slot held round rd, read at
-      // ch = 3 of the round before
+      if constexpr (ch == G::WCH) issue_w(rd + G::WD);  // its slot held round rd, read
+      // at ch = 3 of the round before
       {
         const int sn = s + G::XS - 1;
         issue(sn < S ? sn : S - 1);  // past the end: a harmless refill
