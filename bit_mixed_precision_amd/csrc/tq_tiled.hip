@@ -116,7 +116,8 @@ struct TileGeom {
   static constexpr int kSOff = kWOff + WD * WV * NR * 1024;  // scales: a dword per lane
   static constexpr int kLoop = kSOff + WD * WV * 256;
   static constexpr int kRed = (KG - 1) * NG * MT * NR * 256 * 4;
-  static constexpr int kLds = kLoop > kRed ? kLoop : kRed;
+  static constexpr int kEpi = kRed + BM * (2 * BN + 16);  // partial tiles + fp16 tile
+  static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
   static_assert(NR <= 4, "one scale DMA (64 lanes) covers the weight rows of a wave");
   static_assert(kLds <= 160 * 1024, "the rings fit the LDS of a compute unit");
 };
@@ -358,23 +359,44 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
         for (int e = 0; e < 4; ++e) dst[((i * NR + r) * 4 + e) * 64 + lane] = C[i][r][e];
   }
   __syncthreads();
+  // The k-group sums in fp16, row-major in LDS after the partial tiles (rows
+  // BN + 8 halves apart, so the four rows of a store instruction fall in
+  // different banks), then written out by every wave in 16-byte row chunks
+  // (the MFMA layout would store 2 bytes per lane, 32 bytes per row).
+  constexpr int kRowH = G::BN + 8;
+  uint16_t* stg = reinterpret_cast<uint16_t*>(smem + G::kRed);
   if (wk == 0) {
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const int n = n_base + wn * G::BNW + 16 * r + li;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float sum = C[i][r][e];
 #pragma unroll
           for (int c = 1; c < KG; ++c)
             sum += red[((c - 1) * NG + wn) * kTile + ((i * NR + r) * 4 + e) * 64 + lane];
-          const int m = m_base + 16 * i + 4 * g + e;
-          if (m < M && n < N) Y[(size_t)m * N + n] = f2h_bits(sum);
+          stg[(16 * i + 4 * g + e) * kRowH + wn * G::BNW + 16 * r + li] = f2h_bits(sum);
         }
         __builtin_amdgcn_sched_barrier(0);  // one tile's partial sums at a time
       }
+    }
+  }
+  __syncthreads();
+  constexpr int kChunksRow = G::BN / 8;
+  static_assert((kChunksRow & (kChunksRow - 1)) == 0, "row chunks: a power of two");
+  const bool vec = (N & 7) == 0;  // rows start 16-byte aligned
+  for (int c = threadIdx.x; c < G::BM * kChunksRow; c += 64 * G::WV) {
+    const int row = c / kChunksRow;
+    const int n0 = n_base + 8 * (c % kChunksRow);
+    const int m = m_base + row;
+    if (m >= M || n0 >= N) continue;
+    const uint16_t* src = stg + row * kRowH + (n0 - n_base);
+    uint16_t* dst = Y + (size_t)m * N + n0;
+    if (vec) {
+      *reinterpret_cast<u32x4*>(dst) = *reinterpret_cast<const u32x4*>(src);
+    } else {
+      for (int j = 0; j < 8 && n0 + j < N; ++j) dst[j] = src[j];
     }
   }
 }
