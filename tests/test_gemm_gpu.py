@@ -111,11 +111,14 @@ def test_small_parity(fmt, path, M, N, K):
 # window in which some waves have no block (K = 5120, 9216, 6400), nb not a
 # multiple of the waves per row group, and seven windows (K = 28672); with two
 # m tiles (M = 17 .. 32): windows of 8 blocks, a second m tile of one row
-# (M = 17), and more row groups than the 8 waves of such a workgroup
-# (N = 40000: 10 row groups per CU, run as 8).
+# (M = 17), more row groups than a workgroup of two m tiles takes (N = 40000:
+# 10 row groups per CU, run as 8), and block scales loaded with each pair
+# instead of staged (N = 30000, K = 8448: 8 row groups x 33 blocks is more
+# than four scales per thread; an odd block count leaves the last pair half
+# empty).
 SKINNY_WINDOWS = [(16, 300, 5120), (16, 300, 28672), (9, 8192, 9216), (13, 1000, 6400),
                   (32, 300, 5120), (17, 1000, 6400), (24, 2048, 8192), (32, 2048, 8192),
-                  (20, 40000, 512)]
+                  (20, 40000, 512), (20, 30000, 8448)]
 
 
 @pytest.mark.parametrize("M,N,K", SKINNY_WINDOWS)
