@@ -10,6 +10,11 @@ namespace tq {
 constexpr int kWave = 64;
 constexpr int kBlockK = 256;  // weights per fp16 scale along K
 
+// Fourth word of a raw buffer resource on gfx9-family GPUs (gfx950
+// included): 32-bit data format, no swizzle; loads past the resource's
+// num_records bytes return zero.
+constexpr int kBufferWord3 = 0x00020000;
+
 // Sum over the 64 lanes of a wave; every lane gets the total.
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
