@@ -225,12 +225,24 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 64 * kWavesMt2) void tq2_skinny_ke
   // taking piece g of block 0 for n < 8 and piece 4 + g (block 1) of row
   // n - 8 for n >= 8; load B the same for rows 8..15 with the halves swapped.
   // Block 0 in MFMA order is then A or B by lane, block 1 the other one
-  // rotated by 8 lanes (one DPP move).  Rows past N read row n_base.
+  // rotated by 8 lanes (one DPP move).  The loads are buffer loads: one
+  // resource per wave over its row group (from a valid row: a group past N
+  // reads the tile's last row, and rows past N in a group read its first),
+  // lane offsets fixed for the whole kernel and the pair's offset in a scalar
+  // register, so a load costs no vector instruction (measured 2% faster at
+  // N = 28672, 4-5% for the gate / up product).  With an odd block count the
+  // last pair's second half reads past the row (the next row's bytes, or
+  // zeros past the group's last row) and is never used.
   const uint8_t* wq = up ? qs2 : qs;
   const int ra = 16 * rgo + (li & 7), rb = ra + 8;
   const int pa = li < 8 ? g : 4 + g, pb = li < 8 ? 4 + g : g;
-  const uint8_t* wrowa = wq + (size_t)(n_base + (ra < rows ? ra : 0)) * row_bytes + 16 * pa;
-  const uint8_t* wrowb = wq + (size_t)(n_base + (rb < rows ? rb : 0)) * row_bytes + 16 * pb;
+  const int rg0 = 16 * rgo < rows ? 16 * rgo : rows - 1;
+  const int rin = rows - rg0 < 16 ? rows - rg0 : 16;  // rows of the group in the matrix
+  const auto wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(wq) + (size_t)(n_base + rg0) * row_bytes, 0, rin * (int)row_bytes,
+      kBufferWord3);
+  const int voffa = (ra < rows ? ra - rg0 : 0) * (int)row_bytes + 16 * pa;  // < 2^22
+  const int voffb = (rb < rows ? rb - rg0 : 0) * (int)row_bytes + 16 * pb;
   const int npairs = (nb + 1) >> 1;
   // A operand rows of m tile t: activation rows 16 t + li (rows past M read
   // row M - 1; their results are never written)
@@ -259,17 +271,15 @@ __global__ __launch_bounds__(MT == 1 ? 1024 : 64 * kWavesMt2) void tq2_skinny_ke
   u32x4 wa[P], wb[P];
   uint16_t sbuf[P][2];
 
-  // Weights are read once: non-temporal loads (measured 3-5% faster at
-  // M <= 8 on both layer shapes than plain loads; the TQ1 kernel's 8-byte
-  // loads were slower with the hint, so it keeps plain ones).  Pair c holds
-  // blocks 2c and 2c + 1; with an odd block count the last pair's second half
-  // re-reads its first (never used).
+  // Weights are read once: non-temporal loads (the nt bit of the cache
+  // policy; measured 3-5% faster at M <= 8 on both layer shapes than plain
+  // loads; the TQ1 kernel's 8-byte loads were slower with the hint, so it
+  // keeps plain ones).  Pair c holds blocks 2c and 2c + 1.
   auto load = [&](int d, int c) {
-    const int half2 = 2 * c + 1 < nb ? 64 : 0;
-    const int oa = 128 * c + (pa >= 4 ? half2 - 64 : 0);
-    const int ob = 128 * c + (pb >= 4 ? half2 - 64 : 0);
-    wa[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrowa + oa));
-    wb[d] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrowb + ob));
+    typedef int v4i __attribute__((ext_vector_type(4)));
+    constexpr int kNt = 2;  // cache policy: non-temporal
+    wa[d] = __builtin_bit_cast(u32x4, (v4i)__builtin_amdgcn_raw_buffer_load_b128(wrsrc, voffa, 128 * c, kNt));
+    wb[d] = __builtin_bit_cast(u32x4, (v4i)__builtin_amdgcn_raw_buffer_load_b128(wrsrc, voffb, 128 * c, kNt));
     if constexpr (!STAGE) {
       sbuf[d][0] = srow[2 * c];
       sbuf[d][1] = srow[2 * c + 1 < nb ? 2 * c + 1 : 2 * c];
