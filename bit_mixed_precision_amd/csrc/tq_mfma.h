@@ -128,6 +128,28 @@ struct NaturalConsts {
                                                __builtin_bit_cast(half2v, add[Q]));
     return __builtin_bit_cast(uint32_t, d * __builtin_bit_cast(half2v, s2));
   }
+  // The trit pair (d_{2q}, d_{2q+1}) alone, exact in fp16.
+  template <int Q>
+  __device__ __forceinline__ uint32_t trits(uint32_t z) const {
+    constexpr uint32_t mask = Q == 0 ? 0x000C0003u : 0x00C00030u;
+    const uint32_t v = (z & mask) | magic;
+    const half2v d = __builtin_elementwise_fma(__builtin_bit_cast(half2v, v),
+                                               __builtin_bit_cast(half2v, mul[Q]),
+                                               __builtin_bit_cast(half2v, add[Q]));
+    return __builtin_bit_cast(uint32_t, d);
+  }
+  // B operand of 8 consecutive trits (no scale): the byte pair H of dword x.
+  template <int H>
+  __device__ __forceinline__ half8 trit_operand(uint32_t x) const {
+    const uint32_t z = perm(x, x, H == 0 ? 0x01000100u : 0x03020302u);
+    const uint32_t z2 = z >> 8;
+    u32x4 r;
+    r[0] = trits<0>(z);
+    r[1] = trits<1>(z);
+    r[2] = trits<0>(z2);
+    r[3] = trits<1>(z2);
+    return __builtin_bit_cast(half8, r);
+  }
   // B operand of 8 consecutive weights: the byte pair H (0 or 1) of dword x,
   // times the scale pair s2.
   template <int H>
