@@ -82,12 +82,12 @@ constexpr int64_t kSkinnyLimitM = 32;   // the TQ2 skinny kernel's limit (two m 
 // TQ2 at 17..32 activation rows: the skinny kernel (every workgroup stages
 // all M x K activations, the weights stream once) beats the tiled one where
 // the weight rows per CU are many against the activation rows.  Measured
-// (K = 8192, us skinny / tiled): N = 28672 M = 17 28 / 40, M = 32 35 / 40;
-// N = 16384 M = 20 20.9 / 25.8, M = 32 24.4 / 25.7; N = 8192 M = 17
-// 13.4 / 17.7, M = 24 17.4 / 17.7, M = 32 20.3 / 17.7; N = 4096 M = 20
-// 17.0 / 15.1; K = 28672, N = 8192, M = 17 50.2 / 49.0.
+// (K = 8192, us skinny / tiled): N = 28672 M = 17 28.3 / 33.5, M = 32
+// 35.0 / 35.3; N = 16384 M = 17 18.1 / 23.6, M = 32 23.3 / 23.9; N = 8192
+// M = 17 12.6 / 13.4, M = 20 15.7 / 13.7, M = 32 20.3 / 14.2; N = 4096
+// M = 20 17.0 / 15.1; K = 28672, N = 8192, M = 17 50.2 / 49.0.
 bool tq2_skinny_two_tiles(int64_t M, int64_t N, int64_t K) {
-  return M <= kSkinnyLimitM && K <= 16384 && N >= 384 * M;
+  return M <= kSkinnyLimitM && K <= 16384 && N >= 480 * M;
 }
 
 // The kernel each (format, shape, path) runs.  Shapes are already validated.

@@ -58,7 +58,7 @@ typedef enum {
 } tq_src;
 
 /* Kernel family for tq_gemm_*_ex.  AUTO picks, for TQ2, the skinny kernel for
- * M <= 16, and for M <= 32 when K <= 16384 and N >= 384 M, the tiled MFMA
+ * M <= 16, and for M <= 32 when K <= 16384 and N >= 480 M, the tiled MFMA
  * kernel otherwise; for TQ1, the tiled kernel for M >= 48 with N <= 16384 and
  * the skinny kernel otherwise (measured at K = 8192).  The others force one
  * family (used by the tests to cover both sides of the switch); the TQ2
