@@ -24,10 +24,11 @@
 //    reads 16 B of its row's 64-byte block back, and 4 v_perm_b32 and 4 lane
 //    swaps (v_permlane32_swap / v_permlane16_swap) put them in MFMA B order;
 //    one v_perm_b32 copies a byte pair into both halves, v_and_or_b32 against
-//    the fp16 exponent of 1024 extracts two fields, v_pk_fma_f16 makes them
-//    exact trits and v_pk_mul_f16 applies the block scale (+-s or 0, exact);
-//  * v_mfma_f32_16x16x32_f16 with fp32 accumulators across all of K; one
-//    fp32 -> fp16 rounding writes Y.
+//    the fp16 exponent of 1024 extracts two fields and v_pk_fma_f16 makes
+//    them exact trits;
+//  * v_mfma_f32_16x16x32_f16 with fp32 accumulators: each round's block sums
+//    in its own accumulators and its block scale is applied once per round
+//    (one FMA per element); one fp32 -> fp16 rounding writes Y.
 
 #include <type_traits>
 
@@ -98,7 +99,6 @@ __device__ __forceinline__ void mem_clobber() { asm volatile("" ::: "memory"); }
 template <int MT, int NR, int NG, int KG>
 struct TileGeom {
   static constexpr int WV = NG * KG;  // waves per workgroup
-  static constexpr bool SA = MT * NR <= 8;  // block scale on the accumulators
   static_assert(WV == 4 || WV == 8, "a workgroup is 4 or 8 waves");
   static constexpr int BM = 16 * MT;
   static constexpr int BNW = 16 * NR;  // weight rows per wave
@@ -261,18 +261,18 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int r = 0; r < NR; ++r) C[i][r] = float4v{0.f, 0.f, 0.f, 0.f};
-  // With few MFMAs per decoded operand (MT * NR <= 8) the VALU decode bounds
-  // the loop: the B operands are then the bare trits, a round's block (the
-  // k-group's one 256-weight block) accumulates in Cb, and the block scale
-  // is applied once per round, C += s * Cb (one FMA per accumulator element
-  // instead of a v_pk_mul per 2 weights).  The products are exact either way;
-  // only the fp32 rounding order differs.
-  constexpr bool SA = G::SA;
-  float4v Cb[SA ? MT : 1][SA ? NR : 1];
+  // The B operands are the bare trits; a round's block (the k-group's one
+  // 256-weight block) accumulates in Cb and its scale is applied once per
+  // round, C += s * Cb: one FMA per accumulator element instead of a
+  // v_pk_mul per two weights, whose VALU time bounded the loop of the small
+  // wave tiles (4-8 VALU instructions per MFMA) and held back the larger
+  // ones.  The products are exact either way; only the fp32 rounding order
+  // differs.
+  float4v Cb[MT][NR];
 
   // Weights of round rd in B order and their scale pairs; a k-group without a
   // block in the round (K / 256 not a multiple of KG) gets scale 0, so its
-  // MFMAs add nothing and every wave runs the same straight-line code.
+  // block sum adds nothing and every wave runs the same straight-line code.
   auto read_w = [&](int rd, u32x4* wbo, uint32_t* s2o) {
     const bool active = rd * KG + wk < nb;
 #pragma unroll
@@ -296,13 +296,8 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
   __builtin_amdgcn_s_waitcnt(vmcnt_imm((G::WD - 1) * kWIssue + (G::XS - 1) * G::kPer));
   mem_clobber();
   read_w(0, wb, s2);
-  auto dec = [&](auto hh, uint32_t x, uint32_t sc2) -> half8 {
-    constexpr int H = decltype(hh)::value;
-    if constexpr (SA) return dc.trit_operand<H>(x);
-    else return dc.operand<H>(x, sc2);
-  };
 #pragma unroll
-  for (int r = 0; r < NR; ++r) Bc[r] = dec(std::integral_constant<int, 0>{}, wb[r][0], s2[r]);
+  for (int r = 0; r < NR; ++r) Bc[r] = dc.trit_operand<0>(wb[r][0]);
 
   for (int rd = 0; rd < rounds; ++rd) {
     sfor<0, 4>([&](auto cc) {
@@ -341,14 +336,12 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
       // operands are decoded; then step 1 while the next stage's step 0 is
       half8 B1[NR];
 #pragma unroll
-      for (int r = 0; r < NR; ++r) B1[r] = dec(std::integral_constant<int, 1>{}, wb[r][ch], s2[r]);
+      for (int r = 0; r < NR; ++r) B1[r] = dc.trit_operand<1>(wb[r][ch]);
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          if constexpr (!SA)
-            C[i][r] = mfma16(A[0][i], Bc[r], C[i][r]);
-          else if constexpr (ch == 0)  // a round's first product starts the block's sum
+          if constexpr (ch == 0)  // a round's first product starts the block's sum
             Cb[i][r] = mfma16(A[0][i], Bc[r], float4v{0.f, 0.f, 0.f, 0.f});
           else
             Cb[i][r] = mfma16(A[0][i], Bc[r], Cb[i][r]);
@@ -356,30 +349,23 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         if constexpr (ch < 3)
-          Bc[r] = dec(std::integral_constant<int, 0>{}, wb[r][ch + 1], s2[r]);
+          Bc[r] = dc.trit_operand<0>(wb[r][ch + 1]);
         else
-          Bc[r] = dec(std::integral_constant<int, 0>{}, wnx[r][0], s2n[r]);
+          Bc[r] = dc.trit_operand<0>(wnx[r][0]);
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          if constexpr (SA)
-            Cb[i][r] = mfma16(A[1][i], B1[r], Cb[i][r]);
-          else
-            C[i][r] = mfma16(A[1][i], B1[r], C[i][r]);
-        }
+        for (int r = 0; r < NR; ++r) Cb[i][r] = mfma16(A[1][i], B1[r], Cb[i][r]);
       if constexpr (ch == 3) {
-        if constexpr (SA) {
-          // the block's scale (0 for a k-group without a block this round)
+        // the block's scale (0 for a k-group without a block this round)
 #pragma unroll
-          for (int r = 0; r < NR; ++r) {
-            const float sf = h2f((uint16_t)(s2[r] & 0xffffu));
+        for (int r = 0; r < NR; ++r) {
+          const float sf = h2f((uint16_t)(s2[r] & 0xffffu));
 #pragma unroll
-            for (int i = 0; i < MT; ++i)
+          for (int i = 0; i < MT; ++i)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) C[i][r][e] = __builtin_fmaf(sf, Cb[i][r][e], C[i][r][e]);
-          }
+            for (int e = 0; e < 4; ++e) C[i][r][e] = __builtin_fmaf(sf, Cb[i][r][e], C[i][r][e]);
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
