@@ -336,6 +336,20 @@ int tq_gemm_tq1_tiled(const void* X, const void* qs, int64_t ldq, const void* sc
   return finish(tq::launch_tq1_tiled_shape(t, a, static_cast<hipStream_t>(stream)));
 }
 
+int tq_gemm_tq1_tile(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,
+                     int64_t M, int64_t N, int64_t K, int mt, int nr, int ng, int kg,
+                     void* stream) {
+  bool noop = false;
+  int st = check_gemm(X, qs, scales, Y, M, N, K, true, ldq, &noop);
+  if (st != TQ_OK || noop) return st;
+  const tq::TiledShape t{mt, nr, ng, kg};
+  if (!tq::tiled_compiled(t) || ldq > tq::kTq1TabMaxLdq) return TQ_ERR_UNSUPPORTED;
+  st = device_ready();
+  if (st != TQ_OK) return st;
+  tq::GemmArgs a{X, qs, scales, Y, M, N, K, ldq};
+  return finish(tq::launch_tq1_tab_shape(t, a, static_cast<hipStream_t>(stream)));
+}
+
 int tq_gemm_tq2(const void* X, const void* qs, const void* scales, void* Y, int64_t M, int64_t N,
                 int64_t K, void* stream) {
   return tq_gemm_tq2_ex(X, qs, scales, Y, M, N, K, TQ_PATH_AUTO, stream);

@@ -71,6 +71,12 @@ TiledShape tiled_shape(int64_t M, int64_t N);
 bool tiled_compiled(const TiledShape& t);  // one of the instantiated tiles
 hipError_t launch_tq2_tiled(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_tq2_tiled_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream);
+// The same tiles on 1.6-bit rows (a.ldq bytes each), decoded through an LDS
+// table of byte -> five 2-bit fields; a.ldq <= kTq1TabMaxLdq.
+constexpr int64_t kTq1TabMaxLdq = int64_t(1) << 22;
+bool tq1_tab_scale_in_b(const TiledShape& t);  // block scale folded into the operands
+hipError_t launch_tq1_tab(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_tq1_tab_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream);
 
 // Wide-tile MFMA kernel (v_mfma_f32_32x32x16_f16): a workgroup of 4 waves
 // (ng weight-row groups x kg k-groups) owns 32 mt activation rows x 32 nt ng

@@ -90,13 +90,18 @@ __device__ __forceinline__ void dma2(__amdgpu_buffer_rsrc_t r, int voff, int sof
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 2,
                                            voff, soff, 0, 0);
 }
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, int voff, int soff,
+                                     unsigned char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 4,
+                                           voff, soff, 0, 0);
+}
 
 // Compiler-level memory fence: the barrier intrinsics alone do not keep LDS
 // reads from moving across them, and the LDS writes of the direct copies are
 // not visible to the compiler.
 __device__ __forceinline__ void mem_clobber() { asm volatile("" ::: "memory"); }
 
-template <int MT, int NR, int NG, int KG>
+template <int MT, int NR, int NG, int KG, bool T1 = false>
 struct TileGeom {
   static constexpr int WV = NG * KG;  // waves per workgroup
   static_assert(WV == 4 || WV == 8, "a workgroup is 4 or 8 waves");
@@ -107,7 +112,8 @@ struct TileGeom {
   static constexpr int kStage = KG * kChunk;
   static constexpr int kWRound = WV * (NR * 1024 + 256);  // weights + scales of a round
   // Ring depths: the deepest (XS, WD) whose rings fit the LDS budget.
-  static constexpr int kBudget = WV == 8 ? 160 * 1024 : 80 * 1024;
+  static constexpr int kLut = T1 ? 1024 : 0;  // TQ1: byte -> five 2-bit fields
+  static constexpr int kBudget = (WV == 8 ? 160 * 1024 : 80 * 1024) - kLut;
   static constexpr RingPlan kPlan = ring_plan(kStage, kWRound, kBudget);
   static constexpr int XS = kPlan.xs;
   static constexpr int WD = kPlan.wd;
@@ -123,7 +129,8 @@ struct TileGeom {
   static constexpr int RP = RG8 >= WV ? RG8 / WV : 1;  // distinct row groups per wave
   static constexpr int kWOff = kRing;             // weights: 1 KB per (wave, row group)
   static constexpr int kSOff = kWOff + WD * WV * NR * 1024;  // scales: a dword per lane
-  static constexpr int kLoop = kSOff + WD * WV * 256;
+  static constexpr int kLutOff = kSOff + WD * WV * 256;
+  static constexpr int kLoop = kLutOff + kLut;
   static constexpr int kRed = (KG - 1) * NG * MT * NR * 256 * 4;
   static constexpr int kEpi = kRed + BM * (2 * BN + 16);  // partial tiles + fp16 tile
   static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
@@ -138,14 +145,27 @@ struct TileGeom {
 // m_tile = j / groups, n_tile = 8 (j % groups) + L % 8 with groups =
 // ceil(n_tiles / 8): an XCD walks its weight tiles under one activation tile,
 // which stays in its L2, instead of streaming all of X once per weight tile.
-template <int MT, int NR, int NG, int KG>
-__global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(const uint16_t* __restrict__ X,
-                                                        const uint8_t* __restrict__ qs,
-                                                        const uint16_t* __restrict__ scales,
-                                                        uint16_t* __restrict__ Y, int M, int N,
-                                                        int K, int n_tiles, int m_tiles,
-                                                        int m_outer) {
-  using G = TileGeom<MT, NR, NG, KG>;
+//
+// T1: the weights are 1.6-bit rows (ldq bytes each, five trits per byte).  A
+// round's block b of a row is the bytes floor(256 b / 5) .. floor((256 b +
+// 255) / 5); the direct copy moves the 64 bytes from that first byte rounded
+// down to 4 (16 lanes per row, one dword each), into the slot the 2-bit
+// block would take.  On read-back a lane takes the 14 bytes that hold its 64
+// weights, looks up each byte's five 2-bit fields (d' = d + 1, the 2-bit
+// code's own fields) in a 256-entry LDS table that the workgroup fills with
+// the pages' multiply-by-3 decoder, and shifts the 140-bit field string by
+// the block's trit offset: the four dwords it gets are exactly the 2-bit
+// block's, and the rest of the kernel is unchanged.
+// SB: the block scale multiplies each decoded operand (one v_pk_mul_f16 per
+// two weights, exact) instead of a second accumulator set, which frees the
+// registers the table decode needs in the large wave tiles.
+template <int MT, int NR, int NG, int KG, bool T1, bool SB>
+__device__ __forceinline__ void tiled_body(const uint16_t* __restrict__ X,
+                                           const uint8_t* __restrict__ qs, int ldq,
+                                           const uint16_t* __restrict__ scales,
+                                           uint16_t* __restrict__ Y, int M, int N, int K,
+                                           int n_tiles, int m_tiles, int m_outer) {
+  using G = TileGeom<MT, NR, NG, KG, T1>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int L = blockIdx.x;
   const int j = L >> 3;
@@ -165,10 +185,28 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
   const int nb = K >> 8;
   const int rounds = (nb + KG - 1) / KG;
   const int S = 4 * rounds;  // stages
-  const size_t row_bytes = (size_t)(K >> 2);
+  const size_t row_bytes = T1 ? (size_t)ldq : (size_t)(K >> 2);
 
   NaturalConsts dc;
   dc.init();
+
+  // T1: entry v of the table holds the five 2-bit fields d' of byte value v,
+  // weight j of the byte at bits 2 j .. 2 j + 1, by the multiply-by-3 decoder
+  // (t = 3 q; d' = t >> 8; q = t & 255, most significant digit first).
+  if constexpr (T1) {
+    uint32_t* lut = reinterpret_cast<uint32_t*>(smem + G::kLutOff);
+    for (int v = threadIdx.x; v < 256; v += 64 * G::WV) {
+      uint32_t q = (uint32_t)v, code = 0u;
+#pragma unroll
+      for (int f = 0; f < 5; ++f) {
+        const uint32_t t = 3u * q;
+        code |= (t >> 8) << (2 * f);
+        q = t & 255u;
+      }
+      lut[v] = code;
+    }
+    __syncthreads();
+  }
 
   // ---- activation DMA: instruction q = wave + WV u moves rows 8 rg .. 8 rg + 7
   // (rg = q % RG8) of k-group c = q / RG8's chunk; lane i takes row
@@ -223,11 +261,20 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
   uint32_t woff[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) {
-    const int row = 16 * r + (lane >> 2);
-    const int n = n_base + wn * G::BNW + row;
-    const int rel = n < N ? n - n_base : 0;
-    const int gp = (lane & 3) ^ ((row >> 2) & 3);
-    woff[r] = (uint32_t)rel * (uint32_t)row_bytes + 16u * gp;
+    if constexpr (T1) {
+      // 16 lanes per row, one dword each; instruction t of the 16-row group
+      // adds 4 t rows through the scalar offset.  Rows past N lie past the
+      // resource and read zeros (never written).
+      const int row = 16 * r + (lane >> 4);
+      const int rel = wn * G::BNW + row;
+      woff[r] = (uint32_t)rel * (uint32_t)row_bytes + 4u * (uint32_t)(lane & 15);
+    } else {
+      const int row = 16 * r + (lane >> 2);
+      const int n = n_base + wn * G::BNW + row;
+      const int rel = n < N ? n - n_base : 0;
+      const int gp = (lane & 3) ^ ((row >> 2) & 3);
+      woff[r] = (uint32_t)rel * (uint32_t)row_bytes + 16u * gp;
+    }
   }
   uint32_t soff;
   {
@@ -237,15 +284,29 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
   // Round rd's weights and scales sit in slot rd % WD of their rings.
   auto wdst = [&](int rd) { return G::kWOff + ((rd % G::WD) * G::WV + wave) * NR * 1024; };
   auto sdst = [&](int rd) { return G::kSOff + ((rd % G::WD) * G::WV + wave) * 256; };
+  // The 256-weight block of round rd (past the end: a harmless refill of the
+  // last round's block, which is also what read_w then decodes).
+  auto block_of = [&](int rd) {
+    const int rc = rd < rounds ? rd : rounds - 1;
+    const int b = rc * KG + wk;
+    return b < nb ? b : nb - 1;
+  };
   auto issue_w = [&](int rd) {
-    const int rc = rd < rounds ? rd : rounds - 1;  // past the end: a harmless refill
-    int b = rc * KG + wk;
-    b = b < nb ? b : nb - 1;
+    const int b = block_of(rd);
+    if constexpr (T1) {
+      const int ab = ((256 * b) / 5) & ~3;  // first byte of the block, rounded down to 4
 #pragma unroll
-    for (int r = 0; r < NR; ++r) dma16(wrsrc, (int)woff[r], 64 * b, smem + wdst(rd) + r * 1024);
+      for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          dma4(wrsrc, (int)woff[r], ab + 4 * t * ldq, smem + wdst(rd) + r * 1024 + t * 256);
+    } else {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) dma16(wrsrc, (int)woff[r], 64 * b, smem + wdst(rd) + r * 1024);
+    }
     dma2(srsrc, (int)soff, 2 * b, smem + sdst(rd));
   };
-  constexpr int kWIssue = NR + 1;  // DMA instructions of issue_w
+  constexpr int kWIssue = (T1 ? 4 : 1) * NR + 1;  // DMA instructions of issue_w
   // Read-back offsets: lane (li, g) wants bytes 16 g .. 16 g + 15 of row
   // 16 r + li, and the scale of that row.
   const uint32_t w_rd = li * 64 + 16 * (g ^ ((li >> 2) & 3));
@@ -269,17 +330,67 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
   // ones.  The products are exact either way; only the fp32 rounding order
   // differs.
   float4v Cb[MT][NR];
+  // B operand of 8 weights from byte pair H of dword x: bare trits, or (SB)
+  // trits times the round's scale pair
+  auto operand = [&](auto hh, uint32_t x, uint32_t sc2) -> half8 {
+    constexpr int H = decltype(hh)::value;
+    if constexpr (SB)
+      return dc.template operand<H>(x, sc2);
+    else
+      return dc.template trit_operand<H>(x);
+  };
+  using H0 = std::integral_constant<int, 0>;
+  using H1 = std::integral_constant<int, 1>;
 
   // Weights of round rd in B order and their scale pairs; a k-group without a
   // block in the round (K / 256 not a multiple of KG) gets scale 0, so its
   // block sum adds nothing and every wave runs the same straight-line code.
   auto read_w = [&](int rd, u32x4* wbo, uint32_t* s2o) {
     const bool active = rd * KG + wk < nb;
+    if constexpr (T1) {
+      // Lane (li, g) wants weights 256 b + 64 g .. + 63 of its row: TQ1 bytes
+      // i .. i + 13 (i = floor(x / 5), x = 256 b + 64 g), from trit ph = x - 5 i
+      // of byte i on, i.e. byte o = i - ab of the copied row.
+      const uint32_t b = (uint32_t)block_of(rd);
+      const uint32_t x = 256u * b + 64u * (uint32_t)g;
+      const uint32_t i5 = __umulhi(x, 0xCCCCCCCDu) >> 2;  // floor(x / 5), exact for 32 bits
+      const uint32_t sh = 2u * (x - 5u * i5);               // field offset: 2 ph
+      const uint32_t o = i5 - (((256u * b) / 5u) & ~3u);   // <= 42
+      const uint32_t* lut = reinterpret_cast<const uint32_t*>(smem + G::kLutOff);
+      const uint32_t rdo = (uint32_t)li * 64u + (o & ~3u);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      wbo[r] = to_b_order(*reinterpret_cast<const u32x4*>(smem + wdst(rd) + w_rd + r * 1024));
-      const uint32_t sc = *reinterpret_cast<const uint32_t*>(smem + sdst(rd) + s_rd + 64 * r);
-      s2o[r] = active ? (sc | (sc << 16)) : 0u;
+      for (int r = 0; r < NR; ++r) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(smem + wdst(rd) + r * 1024 + rdo);
+        uint32_t D[5];
+#pragma unroll
+        for (int u = 0; u < 5; ++u) D[u] = src[u];
+        uint32_t E[4];  // bytes o .. o + 15 of the row
+#pragma unroll
+        for (int t = 0; t < 4; ++t) E[t] = __builtin_amdgcn_alignbyte(D[t + 1], D[t], o & 3u);
+        uint32_t c[14];
+#pragma unroll
+        for (int i = 0; i < 14; ++i) c[i] = lut[(E[i >> 2] >> (8 * (i & 3))) & 0xFFu];
+        // the fields of byte i at bits 10 i .. 10 i + 9 of a 160-bit string
+        uint32_t W[5];
+        W[0] = c[0] | (c[1] << 10) | (c[2] << 20) | (c[3] << 30);
+        W[1] = (c[3] >> 2) | (c[4] << 8) | (c[5] << 18) | (c[6] << 28);
+        W[2] = (c[6] >> 4) | (c[7] << 6) | (c[8] << 16) | (c[9] << 26);
+        W[3] = (c[9] >> 6) | (c[10] << 4) | (c[11] << 14) | (c[12] << 24);
+        W[4] = (c[12] >> 8) | (c[13] << 2);
+        u32x4 O;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) O[t] = __builtin_amdgcn_alignbit(W[t + 1], W[t], sh);
+        wbo[r] = to_b_order(O);
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(smem + sdst(rd) + s_rd + 64 * r);
+        s2o[r] = active ? (sc | (sc << 16)) : 0u;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        wbo[r] = to_b_order(*reinterpret_cast<const u32x4*>(smem + wdst(rd) + w_rd + r * 1024));
+        const uint32_t sc = *reinterpret_cast<const uint32_t*>(smem + sdst(rd) + s_rd + 64 * r);
+        s2o[r] = active ? (sc | (sc << 16)) : 0u;
+      }
     }
   };
 
@@ -297,7 +408,7 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
   mem_clobber();
   read_w(0, wb, s2);
 #pragma unroll
-  for (int r = 0; r < NR; ++r) Bc[r] = dc.trit_operand<0>(wb[r][0]);
+  for (int r = 0; r < NR; ++r) Bc[r] = operand(H0{}, wb[r][0], s2[r]);
 
   for (int rd = 0; rd < rounds; ++rd) {
     sfor<0, 4>([&](auto cc) {
@@ -336,12 +447,14 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
       // operands are decoded; then step 1 while the next stage's step 0 is
       half8 B1[NR];
 #pragma unroll
-      for (int r = 0; r < NR; ++r) B1[r] = dc.trit_operand<1>(wb[r][ch]);
+      for (int r = 0; r < NR; ++r) B1[r] = operand(H1{}, wb[r][ch], s2[r]);
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-          if constexpr (ch == 0)  // a round's first product starts the block's sum
+          if constexpr (SB)
+            C[i][r] = mfma16(A[0][i], Bc[r], C[i][r]);
+          else if constexpr (ch == 0)  // a round's first product starts the block's sum
             Cb[i][r] = mfma16(A[0][i], Bc[r], float4v{0.f, 0.f, 0.f, 0.f});
           else
             Cb[i][r] = mfma16(A[0][i], Bc[r], Cb[i][r]);
@@ -349,23 +462,31 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         if constexpr (ch < 3)
-          Bc[r] = dc.trit_operand<0>(wb[r][ch + 1]);
+          Bc[r] = operand(H0{}, wb[r][ch + 1], s2[r]);
         else
-          Bc[r] = dc.trit_operand<0>(wnx[r][0]);
+          Bc[r] = operand(H0{}, wnx[r][0], s2n[r]);
       }
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int r = 0; r < NR; ++r) Cb[i][r] = mfma16(A[1][i], B1[r], Cb[i][r]);
+        for (int r = 0; r < NR; ++r) {
+          if constexpr (SB)
+            C[i][r] = mfma16(A[1][i], B1[r], C[i][r]);
+          else
+            Cb[i][r] = mfma16(A[1][i], B1[r], Cb[i][r]);
+        }
       if constexpr (ch == 3) {
         // the block's scale (0 for a k-group without a block this round)
+        if constexpr (!SB) {
 #pragma unroll
-        for (int r = 0; r < NR; ++r) {
-          const float sf = h2f((uint16_t)(s2[r] & 0xffffu));
+          for (int r = 0; r < NR; ++r) {
+            const float sf = h2f((uint16_t)(s2[r] & 0xffffu));
 #pragma unroll
-          for (int i = 0; i < MT; ++i)
+            for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) C[i][r][e] = __builtin_fmaf(sf, Cb[i][r][e], C[i][r][e]);
+              for (int e = 0; e < 4; ++e)
+                C[i][r][e] = __builtin_fmaf(sf, Cb[i][r][e], C[i][r][e]);
+          }
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
@@ -439,27 +560,64 @@ __global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
   }
 }
 
+// The 2-bit (TQ2) product.
+template <int MT, int NR, int NG, int KG>
+__global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq2_tiled_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ qs,
+    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int M, int N, int K,
+    int n_tiles, int m_tiles, int m_outer) {
+  tiled_body<MT, NR, NG, KG, false, false>(X, qs, 0, scales, Y, M, N, K, n_tiles, m_tiles,
+                                           m_outer);
+}
+
+// The 1.6-bit (TQ1) product on the same tiles, the weights decoded from TQ1
+// bytes through the LDS table (no 2-bit copy of the matrix anywhere).
+template <int MT, int NR, int NG, int KG, bool SB>
+__global__ __launch_bounds__(64 * NG * KG, 8 / (NG * KG)) void tq1_tab_tiled_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ qs, int ldq,
+    const uint16_t* __restrict__ scales, uint16_t* __restrict__ Y, int M, int N, int K,
+    int n_tiles, int m_tiles, int m_outer) {
+  tiled_body<MT, NR, NG, KG, true, SB>(X, qs, ldq, scales, Y, M, N, K, n_tiles, m_tiles,
+                                       m_outer);
+}
+
 // From this many activation tiles on, the m-major order (see the kernel).
 constexpr int64_t kMOuterTiles = 4;
 
-template <int MT, int NR, int NG, int KG>
+// The scale goes into the operands where the wave tile is large (the second
+// accumulator set would not fit beside the table decode).
+constexpr bool t1_scale_in_b(int mt, int nr) { return mt * nr >= 16; }
+
+template <int MT, int NR, int NG, int KG, bool T1 = false>
 hipError_t launch_tiled(const GemmArgs& a, hipStream_t stream) {
-  using G = TileGeom<MT, NR, NG, KG>;
+  using G = TileGeom<MT, NR, NG, KG, T1>;
+  constexpr bool SB = T1 && t1_scale_in_b(MT, NR);
+  const void* fn;
+  if constexpr (T1)
+    fn = reinterpret_cast<const void*>(tq1_tab_tiled_kernel<MT, NR, NG, KG, SB>);
+  else
+    fn = reinterpret_cast<const void*>(tq2_tiled_kernel<MT, NR, NG, KG>);
   static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = lds_limit_once(reinterpret_cast<const void*>(tq2_tiled_kernel<MT, NR, NG, KG>),
-                                G::kLds, lds_set);
+  hipError_t e = lds_limit_once(fn, G::kLds, lds_set);
   if (e != hipSuccess) return e;
   const int64_t n_tiles = (a.N + G::BN - 1) / G::BN;
   const int64_t m_tiles = (a.M + G::BM - 1) / G::BM;
   const int64_t groups = (n_tiles + 7) / 8;
   const int64_t wgs = groups * 8 * m_tiles;
   if (wgs > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((tq2_tiled_kernel<MT, NR, NG, KG>), dim3((unsigned)wgs), dim3(64 * G::WV),
-                     G::kLds,
-                     stream, static_cast<const uint16_t*>(a.X),
-                     static_cast<const uint8_t*>(a.qs), static_cast<const uint16_t*>(a.scales),
-                     static_cast<uint16_t*>(a.Y), (int)a.M, (int)a.N, (int)a.K, (int)n_tiles,
-                     (int)m_tiles, m_tiles >= kMOuterTiles ? 1 : 0);
+  const int m_outer = m_tiles >= kMOuterTiles ? 1 : 0;
+  if constexpr (T1)
+    hipLaunchKernelGGL((tq1_tab_tiled_kernel<MT, NR, NG, KG, SB>), dim3((unsigned)wgs),
+                       dim3(64 * G::WV), G::kLds, stream, static_cast<const uint16_t*>(a.X),
+                       static_cast<const uint8_t*>(a.qs), (int)a.ldq,
+                       static_cast<const uint16_t*>(a.scales), static_cast<uint16_t*>(a.Y),
+                       (int)a.M, (int)a.N, (int)a.K, (int)n_tiles, (int)m_tiles, m_outer);
+  else
+    hipLaunchKernelGGL((tq2_tiled_kernel<MT, NR, NG, KG>), dim3((unsigned)wgs), dim3(64 * G::WV),
+                       G::kLds, stream, static_cast<const uint16_t*>(a.X),
+                       static_cast<const uint8_t*>(a.qs), static_cast<const uint16_t*>(a.scales),
+                       static_cast<uint16_t*>(a.Y), (int)a.M, (int)a.N, (int)a.K, (int)n_tiles,
+                       (int)m_tiles, m_outer);
   return hipGetLastError();
 }
 
@@ -508,18 +666,18 @@ TiledShape tiled_shape(int64_t M, int64_t N) {
   return narrow_wgs <= cus ? TiledShape{2, 2, 1, 8} : TiledShape{2, 2, 1, 4};
 }
 
-template <int MT>
+template <int MT, bool T1>
 hipError_t launch_mt(const TiledShape& t, const GemmArgs& a, hipStream_t stream) {
   if constexpr (MT == 2) {
-    if (t.kg == 8) return t.nr == 2 ? launch_tiled<2, 2, 1, 8>(a, stream)
-                                    : launch_tiled<2, 4, 1, 8>(a, stream);
+    if (t.kg == 8) return t.nr == 2 ? launch_tiled<2, 2, 1, 8, T1>(a, stream)
+                                    : launch_tiled<2, 4, 1, 8, T1>(a, stream);
   }
-  if (t.nr == 2) return t.ng == 2 ? launch_tiled<MT, 2, 2, 4>(a, stream)
-                                  : launch_tiled<MT, 2, 1, 4>(a, stream);
-  if (t.ng == 4) return launch_tiled<MT, 4, 4, 2>(a, stream);
-  if (t.kg == 4) return t.ng == 2 ? launch_tiled<MT, 4, 2, 4>(a, stream)
-                                  : launch_tiled<MT, 4, 1, 4>(a, stream);
-  return launch_tiled<MT, 4, 2, 2>(a, stream);
+  if (t.nr == 2) return t.ng == 2 ? launch_tiled<MT, 2, 2, 4, T1>(a, stream)
+                                  : launch_tiled<MT, 2, 1, 4, T1>(a, stream);
+  if (t.ng == 4) return launch_tiled<MT, 4, 4, 2, T1>(a, stream);
+  if (t.kg == 4) return t.ng == 2 ? launch_tiled<MT, 4, 2, 4, T1>(a, stream)
+                                  : launch_tiled<MT, 4, 1, 4, T1>(a, stream);
+  return launch_tiled<MT, 4, 2, 2, T1>(a, stream);
 }
 
 bool tiled_compiled(const TiledShape& t) {
@@ -534,11 +692,22 @@ bool tiled_compiled(const TiledShape& t) {
 
 hipError_t launch_tq2_tiled_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream) {
   if (t.mt == 8) return launch_tiled<8, 2, 4, 2>(a, stream);
-  return t.mt == 2 ? launch_mt<2>(t, a, stream) : launch_mt<4>(t, a, stream);
+  return t.mt == 2 ? launch_mt<2, false>(t, a, stream) : launch_mt<4, false>(t, a, stream);
 }
 
 hipError_t launch_tq2_tiled(const GemmArgs& a, hipStream_t stream) {
   return launch_tq2_tiled_shape(tiled_shape(a.M, a.N), a, stream);
+}
+
+bool tq1_tab_scale_in_b(const TiledShape& t) { return t1_scale_in_b(t.mt, t.nr); }
+
+hipError_t launch_tq1_tab_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream) {
+  if (t.mt == 8) return launch_tiled<8, 2, 4, 2, true>(a, stream);
+  return t.mt == 2 ? launch_mt<2, true>(t, a, stream) : launch_mt<4, true>(t, a, stream);
+}
+
+hipError_t launch_tq1_tab(const GemmArgs& a, hipStream_t stream) {
+  return launch_tq1_tab_shape(tiled_shape(a.M, a.N), a, stream);
 }
 
 }  // namespace tq

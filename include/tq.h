@@ -334,6 +334,19 @@ int tq_gemm_tq2_wide(const void* X, const void* qs, const void* scales_f16, void
 int tq_gemm_tq1_tiled(const void* X, const void* qs, int64_t ldq, const void* scales_f16, void* Y,
                       int64_t M, int64_t N, int64_t K, int mt, int nw, int kg, void* stream);
 
+/* TQ1 product on the table-decode tiled kernel with an explicit tile, for
+ * tuning and for tests of every tile.  The tiles and their meaning are
+ * tq_gemm_tq2_tile's; the weights are the 1.6-bit rows of tq_gemm_tq1 ("1.6
+ * bits per weight" on the project page "Scaling Laws and Efficient Inference
+ * for Ternary Language Models"), read once from HBM with no 2-bit copy:
+ * each block's bytes are copied to LDS and every byte's five trits come from
+ * a 256-entry table built with the pages' multiply-by-3 decoder.  ldq above
+ * 2^22 or a tile not compiled gives TQ_ERR_UNSUPPORTED.  Everything else is as
+ * tq_gemm_tq1. */
+int tq_gemm_tq1_tile(const void* X, const void* qs, int64_t ldq, const void* scales_f16, void* Y,
+                     int64_t M, int64_t N, int64_t K, int mt, int nr, int ng, int kg,
+                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif
