@@ -68,7 +68,6 @@ SIGNATURES = {
     "tq_transcode_tq1_tq2": (_I, [_P, _I64, _I64, _I64, _P, _P]),
     "tq_tq1_transcode_min_m": (_I64, [_I64, _I64]),
     "tq_gemm_tq1_ws": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _P, _I64, _P]),
-    "tq_gemm_tq1_tiled": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _P]),
     "tq_gemm_tq1_tile": (_I, [_P, _P, _I64, _P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P]),
     "tq_pack_dev_workspace_bytes": (_I64, [_I64, _I64]),
     "tq_pack_tq2_dev": (_I, [_P, _I64, _I64, C.c_double, _P, _P, _P, _P, _P, _I64, _P]),
@@ -441,17 +440,6 @@ def tq_gemm_tq2_wide(X, qs, scales, mt: int, nt: int, ng: int, kg: int, Y=None, 
     with _device_of(X):
         _check(lib.tq_gemm_tq2_wide(_ptr(X), _ptr(qs), _ptr(scales), _ptr(Y), M, N, K, mt, nt, ng,
                                     kg, _stream(stream, X.device)), where)
-    return Y
-
-
-def tq_gemm_tq1_tiled(X, qs, scales, mt: int, nw: int, kg: int, Y=None, stream=None):
-    """tq_gemm_tq1 on the tiled kernel with an explicit (mt, nw, kg) tile."""
-    where = "tq_gemm_tq1_tiled"
-    M, N, K, ldq = _gemm_operands(X, qs, scales, where, ldq_from_qs=True)
-    Y = _out(Y, M, N, where, (("X", X), ("qs", qs), ("scales", scales)))
-    with _device_of(X):
-        _check(lib.tq_gemm_tq1_tiled(_ptr(X), _ptr(qs), ldq, _ptr(scales), _ptr(Y), M, N, K, mt,
-                                     nw, kg, _stream(stream, X.device)), where)
     return Y
 
 

@@ -21,12 +21,14 @@ constexpr int64_t kMaxLdq = int64_t(1) << 24;
 // so that every byte offset fits the kernel's 32-bit buffer offsets.
 constexpr int64_t kMaxSteElems = int64_t(1) << 30;
 // Activation rows from which a TQ1 product with a workspace transcodes the
-// weights once and runs the TQ2 kernels.  The TQ1 kernels cost a step per 16
-// (skinny) or 32 rows (two slices); the transcoding a fixed read and write of
-// the matrix.  Measured at K = 8192: cheaper from 17 rows at N = 8192 (29.5
-// against 35.7 us at M = 24) and from 33 at N = 28672 (74.9 against 98.1 us
-// at M = 40; 64.6 against 58.3 us at M = 32).
-int64_t tq1_transcode_min_m(int64_t N) { return N <= 16384 ? 17 : 33; }
+// weights once and runs the TQ2 kernels, instead of the table-decode tiled
+// kernel (which reads the TQ1 bytes once and needs no workspace; its LDS
+// table lookups cost it 25-55% over the TQ2 kernel on the same tile, the
+// transcoding a read and a write of the matrix).  Measured at K = 8192 (us,
+// table kernel / transcode + TQ2): N = 8192 M = 32 19.8 / 22.6, M = 64
+// 27.8 / 28.6, M = 128 36.6 / 35.4; N = 28672 M = 32 47.0 / 47.4, M = 48
+// 66.6 / 59.1, M = 64 67.2 / 62.4, M = 128 85.5 / 84.8.
+int64_t tq1_transcode_min_m(int64_t N) { return N <= 16384 ? 96 : 33; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -94,7 +96,7 @@ bool tq2_skinny_two_tiles(int64_t M, int64_t N, int64_t K) {
 Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
   if (path == TQ_PATH_AUTO) {
     if (tq1)
-      path = M > kSkinnyMaxM && tq::tq1_prefers_tiled(M, N) ? TQ_PATH_TILED : TQ_PATH_SKINNY;
+      path = M > kSkinnyMaxM ? TQ_PATH_TILED : TQ_PATH_SKINNY;
     else
       path = M <= kSkinnyMaxM || tq2_skinny_two_tiles(M, N, K) ? TQ_PATH_SKINNY : TQ_PATH_TILED;
   }
@@ -113,9 +115,9 @@ Choice choose(bool tq1, int64_t M, int64_t N, int64_t K, int path) {
                     tq::skinny_ring_first(M, K) ? 1 : 0};
     case TQ_PATH_TILED: {
       if (tq1) {
-        const tq::Tq1TiledShape t = tq::tq1_tiled_shape(M, N);
-        return Choice{tq::launch_tq1_tiled, "tq1_tiled_kernel", t.mt, t.nw, t.kg,
-                      tq::tq1_tiled_depth(), tq::tq1_tiled_xahead(t)};
+        const tq::TiledShape t = tq::tq1_tab_shape(M, N);
+        return Choice{tq::launch_tq1_tab, "tq1_tab_tiled_kernel", t.mt, t.nr, t.ng, t.kg,
+                      tq::tq1_tab_scale_in_b(t) ? 1 : 0};
       }
       const tq::TiledShape t = tq::tiled_shape(M, N);
       return Choice{tq::launch_tq2_tiled, "tq2_tiled_kernel", t.mt, t.nr, t.ng, t.kg};
@@ -211,6 +213,9 @@ int tq_kernel_name(int format, int64_t M, int64_t N, int64_t K, int path, char* 
   else if (c.variant2 >= 0 && c.launch == tq::launch_tq2_skinny)  // plain product: GLU = false
     snprintf(buf, sizeof buf, "%s<%d, %s, false, %d, %s>", c.name, c.variant,
              c.variant2 ? "true" : "false", c.variant3, c.variant4 ? "true" : "false");
+  else if (c.launch == tq::launch_tq1_tab)  // last argument: scale in the operands
+    snprintf(buf, sizeof buf, "%s<%d, %d, %d, %d, %s>", c.name, c.variant, c.variant2,
+             c.variant3, c.variant4, c.variant5 ? "true" : "false");
   else if (c.variant5 >= 0)
     snprintf(buf, sizeof buf, "%s<%d, %d, %d, %d, %d>", c.name, c.variant, c.variant2,
              c.variant3, c.variant4, c.variant5);
@@ -321,19 +326,6 @@ int tq_gemm_tq2_wide(const void* X, const void* qs, const void* scales, void* Y,
   if (st != TQ_OK) return st;
   tq::GemmArgs a{X, qs, scales, Y, M, N, K, 0};
   return finish(tq::launch_tq2_wide_shape(w, a, static_cast<hipStream_t>(stream)));
-}
-
-int tq_gemm_tq1_tiled(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,
-                      int64_t M, int64_t N, int64_t K, int mt, int nw, int kg, void* stream) {
-  bool noop = false;
-  int st = check_gemm(X, qs, scales, Y, M, N, K, true, ldq, &noop);
-  if (st != TQ_OK || noop) return st;
-  const tq::Tq1TiledShape t{mt, nw, kg};
-  if (!tq::tq1_tiled_compiled(t)) return TQ_ERR_UNSUPPORTED;
-  st = device_ready();
-  if (st != TQ_OK) return st;
-  tq::GemmArgs a{X, qs, scales, Y, M, N, K, ldq};
-  return finish(tq::launch_tq1_tiled_shape(t, a, static_cast<hipStream_t>(stream)));
 }
 
 int tq_gemm_tq1_tile(const void* X, const void* qs, int64_t ldq, const void* scales, void* Y,

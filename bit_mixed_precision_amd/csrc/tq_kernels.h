@@ -75,6 +75,7 @@ hipError_t launch_tq2_tiled_shape(const TiledShape& t, const GemmArgs& a, hipStr
 // table of byte -> five 2-bit fields; a.ldq <= kTq1TabMaxLdq.
 constexpr int64_t kTq1TabMaxLdq = int64_t(1) << 22;
 bool tq1_tab_scale_in_b(const TiledShape& t);  // block scale folded into the operands
+TiledShape tq1_tab_shape(int64_t M, int64_t N);  // the automatic tile
 hipError_t launch_tq1_tab(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_tq1_tab_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream);
 
@@ -87,19 +88,6 @@ struct WideShape {
 bool wide_compiled(const WideShape& w);
 bool wide_fits(int64_t M, int64_t N, int64_t K);  // 32-bit buffer offsets suffice
 hipError_t launch_tq2_wide_shape(const WideShape& w, const GemmArgs& a, hipStream_t stream);
-
-// Tiled MFMA kernel for TQ1 and M > 16: a workgroup of nw x kg waves (kg of
-// them split K) owns 16 mt activation rows x 16 nw weight rows.
-struct Tq1TiledShape {
-  int mt, nw, kg;
-};
-Tq1TiledShape tq1_tiled_shape(int64_t M, int64_t N);
-bool tq1_prefers_tiled(int64_t M, int64_t N);  // the automatic choice for M > 16
-bool tq1_tiled_compiled(const Tq1TiledShape& t);
-int tq1_tiled_depth();                           // weight ring depth in stages
-int tq1_tiled_xahead(const Tq1TiledShape& t);    // stages the activations are loaded ahead
-hipError_t launch_tq1_tiled(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_tq1_tiled_shape(const Tq1TiledShape& t, const GemmArgs& a, hipStream_t stream);
 
 // Plain streaming read of `bytes` (a multiple of 16) at src; sink gets a
 // write only if the folded data equals one fixed value.

@@ -114,12 +114,20 @@ struct TileGeom {
   // Ring depths: the deepest (XS, WD) whose rings fit the LDS budget.
   static constexpr int kLut = T1 ? 1024 : 0;  // TQ1: byte -> five 2-bit fields
   static constexpr int kBudget = (WV == 8 ? 160 * 1024 : 80 * 1024) - kLut;
+  // (A second weight slot in place of a fourth activation stage, which lets
+  // the 1.6-bit decode spread over the whole round, measured slower for it:
+  // M = 128, K = 8192, N = 28672 85.5 -> 90.5 us, N = 8192 36.6 -> 40.0 us.)
   static constexpr RingPlan kPlan = ring_plan(kStage, kWRound, kBudget);
   static constexpr int XS = kPlan.xs;
   static constexpr int WD = kPlan.wd;
   static constexpr int WCH = w_issue_ch(WD);  // stage of a round that issues weights
   static_assert(XS <= 4 * WD - WCH, "weights must arrive before the stage that reads them");
   static_assert(XS <= 6, "round 0 is the only round whose wait window reaches the prologue");
+  // T1: row group r of the next round's weights is decoded at stage wch_of(r)
+  // of the round, spread over the stages from the first at which they have
+  // landed
+  static constexpr int kWReady = w_ready_ch(XS, WD);
+  static constexpr int wch_of(int r) { return kWReady + r * (4 - kWReady) / NR; }
   static constexpr int kRing = XS * kStage;
   static constexpr int RG8 = BM / 8;          // 8-row DMA groups per chunk
   static constexpr int kXfer = KG * RG8;      // DMA instructions per stage
@@ -345,45 +353,48 @@ __device__ __forceinline__ void tiled_body(const uint16_t* __restrict__ X,
   // Weights of round rd in B order and their scale pairs; a k-group without a
   // block in the round (K / 256 not a multiple of KG) gets scale 0, so its
   // block sum adds nothing and every wave runs the same straight-line code.
+  // T1: row group r of round rd's weights, decoded from the copied TQ1 bytes.
+  auto read_w_row = [&](int rd, int r, u32x4* wbo, uint32_t* s2o) {
+    const bool active = rd * KG + wk < nb;
+    // Lane (li, g) wants weights 256 b + 64 g .. + 63 of its row: TQ1 bytes
+    // i .. i + 13 (i = floor(x / 5), x = 256 b + 64 g), from trit ph = x - 5 i
+    // of byte i on, i.e. byte o = i - ab of the copied row.
+    const uint32_t b = (uint32_t)block_of(rd);
+    const uint32_t x = 256u * b + 64u * (uint32_t)g;
+    const uint32_t i5 = __umulhi(x, 0xCCCCCCCDu) >> 2;  // floor(x / 5), exact for 32 bits
+    const uint32_t sh = 2u * (x - 5u * i5);               // field offset: 2 ph
+    const uint32_t o = i5 - (((256u * b) / 5u) & ~3u);   // <= 42
+    const uint32_t* lut = reinterpret_cast<const uint32_t*>(smem + G::kLutOff);
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(smem + wdst(rd) + r * 1024 +
+                                                            (uint32_t)li * 64u + (o & ~3u));
+    uint32_t D[5];
+#pragma unroll
+    for (int u = 0; u < 5; ++u) D[u] = src[u];
+    uint32_t E[4];  // bytes o .. o + 15 of the row
+#pragma unroll
+    for (int t = 0; t < 4; ++t) E[t] = __builtin_amdgcn_alignbyte(D[t + 1], D[t], o & 3u);
+    uint32_t c[14];
+#pragma unroll
+    for (int i = 0; i < 14; ++i) c[i] = lut[(E[i >> 2] >> (8 * (i & 3))) & 0xFFu];
+    // the fields of byte i at bits 10 i .. 10 i + 9 of a 160-bit string
+    uint32_t W[5];
+    W[0] = c[0] | (c[1] << 10) | (c[2] << 20) | (c[3] << 30);
+    W[1] = (c[3] >> 2) | (c[4] << 8) | (c[5] << 18) | (c[6] << 28);
+    W[2] = (c[6] >> 4) | (c[7] << 6) | (c[8] << 16) | (c[9] << 26);
+    W[3] = (c[9] >> 6) | (c[10] << 4) | (c[11] << 14) | (c[12] << 24);
+    W[4] = (c[12] >> 8) | (c[13] << 2);
+    u32x4 O;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) O[t] = __builtin_amdgcn_alignbit(W[t + 1], W[t], sh);
+    wbo[r] = to_b_order(O);
+    const uint32_t sc = *reinterpret_cast<const uint32_t*>(smem + sdst(rd) + s_rd + 64 * r);
+    s2o[r] = active ? (sc | (sc << 16)) : 0u;
+  };
   auto read_w = [&](int rd, u32x4* wbo, uint32_t* s2o) {
     const bool active = rd * KG + wk < nb;
     if constexpr (T1) {
-      // Lane (li, g) wants weights 256 b + 64 g .. + 63 of its row: TQ1 bytes
-      // i .. i + 13 (i = floor(x / 5), x = 256 b + 64 g), from trit ph = x - 5 i
-      // of byte i on, i.e. byte o = i - ab of the copied row.
-      const uint32_t b = (uint32_t)block_of(rd);
-      const uint32_t x = 256u * b + 64u * (uint32_t)g;
-      const uint32_t i5 = __umulhi(x, 0xCCCCCCCDu) >> 2;  // floor(x / 5), exact for 32 bits
-      const uint32_t sh = 2u * (x - 5u * i5);               // field offset: 2 ph
-      const uint32_t o = i5 - (((256u * b) / 5u) & ~3u);   // <= 42
-      const uint32_t* lut = reinterpret_cast<const uint32_t*>(smem + G::kLutOff);
-      const uint32_t rdo = (uint32_t)li * 64u + (o & ~3u);
 #pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(smem + wdst(rd) + r * 1024 + rdo);
-        uint32_t D[5];
-#pragma unroll
-        for (int u = 0; u < 5; ++u) D[u] = src[u];
-        uint32_t E[4];  // bytes o .. o + 15 of the row
-#pragma unroll
-        for (int t = 0; t < 4; ++t) E[t] = __builtin_amdgcn_alignbyte(D[t + 1], D[t], o & 3u);
-        uint32_t c[14];
-#pragma unroll
-        for (int i = 0; i < 14; ++i) c[i] = lut[(E[i >> 2] >> (8 * (i & 3))) & 0xFFu];
-        // the fields of byte i at bits 10 i .. 10 i + 9 of a 160-bit string
-        uint32_t W[5];
-        W[0] = c[0] | (c[1] << 10) | (c[2] << 20) | (c[3] << 30);
-        W[1] = (c[3] >> 2) | (c[4] << 8) | (c[5] << 18) | (c[6] << 28);
-        W[2] = (c[6] >> 4) | (c[7] << 6) | (c[8] << 16) | (c[9] << 26);
-        W[3] = (c[9] >> 6) | (c[10] << 4) | (c[11] << 14) | (c[12] << 24);
-        W[4] = (c[12] >> 8) | (c[13] << 2);
-        u32x4 O;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) O[t] = __builtin_amdgcn_alignbit(W[t + 1], W[t], sh);
-        wbo[r] = to_b_order(O);
-        const uint32_t sc = *reinterpret_cast<const uint32_t*>(smem + sdst(rd) + s_rd + 64 * r);
-        s2o[r] = active ? (sc | (sc << 16)) : 0u;
-      }
+      for (int r = 0; r < NR; ++r) read_w_row(rd, r, wbo, s2o);
     } else {
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
@@ -433,7 +444,15 @@ __device__ __forceinline__ void tiled_body(const uint16_t* __restrict__ X,
 #pragma unroll
         for (int i = 0; i < MT; ++i)
           A[h][i] = *reinterpret_cast<const half8*>(base + (a_off0 ^ (64u * h)) + 2048 * i);
-      if constexpr (ch == 3) read_w(rd + 1, wnx, s2n);  // stale refill past the end
+      if constexpr (T1) {
+        // the next round's row groups, each in its own stage of this round
+        sfor<0, NR>([&](auto rr) {
+          constexpr int r = decltype(rr)::value;
+          if constexpr (G::wch_of(r) == ch) read_w_row(rd + 1, r, wnx, s2n);
+        });
+      } else if constexpr (ch == 3) {
+        read_w(rd + 1, wnx, s2n);  // stale refill past the end
+      }
       // all LDS reads of the stage are in flight before any of them is used
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (ch == G::WCH) issue_w(rd + G::WD);  // its slot held round rd, read
@@ -701,13 +720,26 @@ hipError_t launch_tq2_tiled(const GemmArgs& a, hipStream_t stream) {
 
 bool tq1_tab_scale_in_b(const TiledShape& t) { return t1_scale_in_b(t.mt, t.nr); }
 
+// The 1.6-bit tiles: those of the 2-bit product, except that where that takes
+// 32 activation rows x 64 weight rows past M = 32 (fewer compute units than
+// its 64 x 128 tiles need) the table decode prefers 64 x 32 tiles, which
+// decode each weight once per 64 activation rows (K = 8192, N = 8192, M = 64:
+// 26.7 against 32.2 us).
+TiledShape tq1_tab_shape(int64_t M, int64_t N) {
+  const TiledShape t = tiled_shape(M, N);
+  if (M > 32 && t.mt == 2 && t.nr == 4) return TiledShape{4, 2, 1, 4};
+  return t;
+}
+
 hipError_t launch_tq1_tab_shape(const TiledShape& t, const GemmArgs& a, hipStream_t stream) {
   if (t.mt == 8) return launch_tiled<8, 2, 4, 2, true>(a, stream);
   return t.mt == 2 ? launch_mt<2, true>(t, a, stream) : launch_mt<4, true>(t, a, stream);
 }
 
 hipError_t launch_tq1_tab(const GemmArgs& a, hipStream_t stream) {
-  return launch_tq1_tab_shape(tiled_shape(a.M, a.N), a, stream);
+  // 32-bit row offsets within a tile: larger row strides take the skinny kernel
+  if (a.ldq > kTq1TabMaxLdq) return launch_tq1_skinny(a, stream);
+  return launch_tq1_tab_shape(tq1_tab_shape(a.M, a.N), a, stream);
 }
 
 }  // namespace tq

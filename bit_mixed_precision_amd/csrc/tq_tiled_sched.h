@@ -33,6 +33,14 @@ constexpr RingPlan ring_plan(int stage_bytes, int round_bytes, int budget) {
   return RingPlan{3, 1};
 }
 
+// First stage of a round (ch) at whose wait the weights of the next round
+// have landed: they were issued at ch = wch of round rd + 1 - wd, and the wait
+// of stage s covers every DMA issued up to iteration s - xs + 1.
+constexpr int w_ready_ch(int xs, int wd) {
+  const int c = 4 * (1 - wd) + w_issue_ch(wd) + xs - 1;
+  return c < 0 ? 0 : c;
+}
+
 // Instructions a wave may leave outstanding at the wait of stage s = 4 rd + ch
 // such that stage s's activation DMA (and round rd + 1's weights at ch = 3)
 // have landed: the activation DMAs of the xs - 2 stages after stage s, plus

@@ -59,10 +59,12 @@ typedef enum {
 
 /* Kernel family for tq_gemm_*_ex.  AUTO picks, for TQ2, the skinny kernel for
  * M <= 16, and for M <= 32 when K <= 16384 and N >= 480 M, the tiled MFMA
- * kernel otherwise; for TQ1, the tiled kernel for M >= 48 with N <= 16384 and
- * the skinny kernel otherwise (measured at K = 8192).  The others force one
+ * kernel otherwise; for TQ1, the skinny kernel for M <= 16 and the tiled
+ * (table-decode) kernel above (measured at K = 8192).  The others force one
  * family (used by the tests to cover both sides of the switch); the TQ2
- * skinny family serves M <= 32 and returns TQ_ERR_UNSUPPORTED above. */
+ * skinny family serves M <= 32 and returns TQ_ERR_UNSUPPORTED above.  The
+ * TQ1 tiled family takes ldq <= 2^22; a larger row stride runs the skinny
+ * kernel instead. */
 typedef enum {
   TQ_PATH_AUTO = 0,
   TQ_PATH_SKINNY = 1,
@@ -276,7 +278,8 @@ int tq_transcode_tq1_tq2(const void* qs1, int64_t ldq, int64_t N, int64_t K, voi
                          void* stream);
 
 /* Activation rows from which tq_gemm_tq1_ws transcodes for an N x K matrix
- * (the measured crossover: 17 for N <= 16384, else 33); TQ_ERR_SHAPE for
+ * (the measured crossover against the table-decode tiled kernel: 96 for
+ * N <= 16384, else 33); TQ_ERR_SHAPE for
  * N < 1 or K not a positive multiple of 256. */
 int64_t tq_tq1_transcode_min_m(int64_t N, int64_t K);
 
@@ -284,8 +287,10 @@ int64_t tq_tq1_transcode_min_m(int64_t N, int64_t K);
  * M >= tq_tq1_transcode_min_m(N, K) and workspace_bytes >= tq_tq2_bytes(N, K),
  * the weights are first re-packed into the workspace as by
  * tq_transcode_tq1_tq2 and the TQ2 kernels of tq_gemm_tq2 run on it (the
- * TQ1 kernels decode every weight once per activation tile; this decodes it
- * once per call), so Y equals tq_gemm_tq2's on the same trits bit for bit.
+ * TQ1 tiled kernel decodes every weight through LDS table lookups once per
+ * activation tile; this decodes it once per call, at the cost of writing and
+ * reading a 2-bit copy), so Y equals tq_gemm_tq2's on the same trits bit for
+ * bit.
  * Otherwise (smaller M, no or too small a workspace) it is tq_gemm_tq1.
  * The workspace is device memory owned by the caller, 16-byte aligned when
  * given (TQ_ERR_ALIGN otherwise), overwritten by the call, and must not
@@ -325,14 +330,6 @@ int tq_gemm_tq2_tile(const void* X, const void* qs, const void* scales_f16, void
  * Everything else is as tq_gemm_tq2. */
 int tq_gemm_tq2_wide(const void* X, const void* qs, const void* scales_f16, void* Y, int64_t M,
                      int64_t N, int64_t K, int mt, int nt, int ng, int kg, void* stream);
-
-/* TQ1 product on the tiled kernel with an explicit tile, for tuning and for
- * tests of every tile: 16 mt activation rows x 16 nw weight rows per
- * workgroup of nw x kg waves (kg of them split K).  Compiled tiles: (mt, nw,
- * kg) in {(1, 4, 4), (2, 4, 2), (2, 4, 4), (4, 4, 1), (4, 4, 2), (2, 8, 2)};
- * any other gives TQ_ERR_UNSUPPORTED.  Everything else is as tq_gemm_tq1. */
-int tq_gemm_tq1_tiled(const void* X, const void* qs, int64_t ldq, const void* scales_f16, void* Y,
-                      int64_t M, int64_t N, int64_t K, int mt, int nw, int kg, void* stream);
 
 /* TQ1 product on the table-decode tiled kernel with an explicit tile, for
  * tuning and for tests of every tile.  The tiles and their meaning are

@@ -105,18 +105,21 @@ def test_tile_errors():
     assert _gt4(3, 2, 1, 4, X=None, M=0) == tq.TQ_OK
 
 
-def _gt1(mt, nw, kg, X=A, M=40, K=512, ldq=112):
-    return tq.raw_call("tq_gemm_tq1_tiled", X, A, ldq, A, A, M, 64, K, mt, nw, kg, None)
+def _gt1(mt, nr, ng, kg, X=A, M=40, K=512, ldq=112):
+    return tq.raw_call("tq_gemm_tq1_tile", X, A, ldq, A, A, M, 64, K, mt, nr, ng, kg, None)
 
 
-def test_tq1_tiled_tile_errors():
-    assert _gt1(2, 4, 4, X=None) == tq.TQ_ERR_NULL
-    assert _gt1(2, 4, 4, K=300) == tq.TQ_ERR_SHAPE
-    assert _gt1(2, 4, 4, ldq=96) == tq.TQ_ERR_SHAPE  # < ceil(512/5)
-    for tile in [(3, 4, 4), (8, 4, 1), (1, 8, 2), (2, 8, 4), (4, 2, 2), (0, 4, 4), (2, 4, 3),
-                 (2, 4, 1)]:
+def test_tq1_tile_errors():
+    # argument checks, then the tile and the table kernel's row-stride limit,
+    # all before any device work
+    assert _gt1(2, 2, 1, 4, X=None) == tq.TQ_ERR_NULL
+    assert _gt1(2, 2, 1, 4, K=300) == tq.TQ_ERR_SHAPE
+    assert _gt1(2, 2, 1, 4, ldq=96) == tq.TQ_ERR_SHAPE  # < ceil(512/5)
+    for tile in [(2, 2, 4, 2), (2, 2, 2, 2), (2, 3, 1, 4), (8, 4, 4, 2), (4, 1, 1, 4),
+                 (3, 2, 1, 4), (4, 2, 1, 8), (4, 4, 1, 8), (2, 4, 2, 8)]:
         assert _gt1(*tile) == tq.TQ_ERR_UNSUPPORTED, tile
-    assert _gt1(3, 4, 4, X=None, M=0) == tq.TQ_OK
+    assert _gt1(2, 2, 1, 4, ldq=(1 << 22) + 16) == tq.TQ_ERR_UNSUPPORTED
+    assert _gt1(3, 2, 1, 4, X=None, M=0) == tq.TQ_OK
 
 
 def test_pack_dev_argument_errors():
@@ -255,7 +258,7 @@ def test_transcode_argument_errors():
 
 
 def test_gemm_tq1_ws_argument_errors():
-    assert tq.tq_tq1_transcode_min_m(8192, 8192) == 17
+    assert tq.tq_tq1_transcode_min_m(8192, 8192) == 96
     assert tq.tq_tq1_transcode_min_m(28672, 8192) == 33
     assert tq.raw_call("tq_tq1_transcode_min_m", 0, 8192) == tq.TQ_ERR_SHAPE
     assert tq.raw_call("tq_tq1_transcode_min_m", 16, 300) == tq.TQ_ERR_SHAPE
@@ -273,7 +276,7 @@ def test_ldq_upper_bound():
     big = (1 << 24) + 16
     assert _g1(ldq=big) == tq.TQ_ERR_SHAPE
     assert _g1(ldq=1 << 31) == tq.TQ_ERR_SHAPE
-    assert tq.raw_call("tq_gemm_tq1_tiled", A, A, big, A, A, 40, 64, 512, 2, 4, 4,
+    assert tq.raw_call("tq_gemm_tq1_tile", A, A, big, A, A, 40, 64, 512, 2, 2, 1, 4,
                        None) == tq.TQ_ERR_SHAPE
     assert tq.raw_call("tq_transcode_tq1_tq2", A, big, 4, 8192, A, None) == tq.TQ_ERR_SHAPE
     assert tq.raw_call("tq_gemm_tq1_ws", A, A, big, A, A, 64, 16, 256, A, 1 << 20,
@@ -316,7 +319,7 @@ def test_binding_rejects_bad_gemm_tensors():
     _raises(tq.TQ_ERR_DEVICE, tq.tq_gemm_tq1, X, q1, s)
     _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq1, X, q1, _t((32, 4), "float16"))
     _raises(tq.TQ_ERR_VALUE, tq.tq_gemm_tq1, X, q1.half(), s)
-    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq1_tiled, X, q1, _t((16, 2), "float16"), 2, 4, 4)
+    _raises(tq.TQ_ERR_SHAPE, tq.tq_gemm_tq1_tile, X, q1, _t((16, 2), "float16"), 2, 2, 1, 4)
     _raises(tq.TQ_ERR_DEVICE, tq.tq_gemm_tq1_ws, X, q1, s, _t((32 * 128,), "uint8"))
     _raises(tq.TQ_ERR_VALUE, tq.tq_gemm_tq1_ws, X, q1, s, _t((32 * 128,), "int32"))
 

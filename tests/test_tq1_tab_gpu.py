@@ -117,3 +117,17 @@ def test_tq1_tab_full_size_every_column(N):
         tq.tq_gemm_tq1_tile(dev(X), qd, sd, *tile, Y)
         torch.cuda.synchronize()
         check_close(Y.cpu().numpy(), R(X), f"tq1 tab full N={N} M={M}")
+
+
+def test_tq1_auto_large_row_stride_runs_skinny():
+    """ldq past 2^22 (a 4 MiB row stride): the automatic choice at M > 16
+    takes the skinny kernel, whose offsets allow it, and stays exact to the
+    bar; the explicit table-kernel entry refuses it."""
+    M, N, K = 40, 16, 512
+    ldq = (1 << 22) + 16
+    T, s = iid_problem(N, K, 0.31, 25)
+    X = activations(M, K, 25)
+    q = tq.tq_pack_tq1(T, ldq=ldq)[0]
+    Y = tq.tq_gemm_tq1(dev(X), dev(q), dev(s))
+    torch.cuda.synchronize()
+    check_close(Y.cpu().numpy(), ref(X, T, s), "tq1 auto, ldq = 2^22 + 16")
