@@ -33,6 +33,9 @@ SHAPES = [(8192, 8192), (8192, 28672)]  # (K, N)
 TQ2_MS = [1, 2, 4, 8, 16, 32, 64, 128]
 TQ1_MS = [1, 4, 16, 64]
 RING_BYTES = 1 << 30
+# TQ1 batch calls take the workspace product from its switch point on
+# (--no-workspace: every TQ1 call through tq_gemm_tq1, which needs none)
+USE_WORKSPACE = True
 
 
 def tq1_ldq(K):
@@ -83,6 +86,10 @@ def prefill_calls():
     return [(fmt, M, N, K) for fmt in ("tq2", "tq1") for K, N in SHAPES for M in PREFILL_MS]
 
 
+def tq1_uses_workspace(tq, M, N, K):
+    return USE_WORKSPACE and M >= tq.tq_tq1_transcode_min_m(N, K)
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -123,7 +130,7 @@ def build_inputs(torch, tq, calls):
             xs[xin] = torch.from_numpy(activations_fp16(seed_for(501, *xin), *xin)).cuda()
         if yout not in ys:
             ys[yout] = torch.empty(yout, dtype=torch.float16, device="cuda")
-        if fmt == "tq1" and M >= tq.tq_tq1_transcode_min_m(N, K) and ("ws", N, K) not in xs:
+        if fmt == "tq1" and tq1_uses_workspace(tq, M, N, K) and ("ws", N, K) not in xs:
             xs[("ws", N, K)] = torch.empty(N * K // 4, dtype=torch.uint8, device="cuda")
     return rings, xs, ys
 
@@ -149,7 +156,7 @@ def run_call(tq, fmt, M, N, K, rings, xs, ys, stream):
     if fmt == "tq2":
         st = tq.lib.tq_gemm_tq2(X.data_ptr(), q.data_ptr(), s.data_ptr(), Y.data_ptr(), M, N, K,
                                 stream)
-    elif M >= tq.tq_tq1_transcode_min_m(N, K):
+    elif tq1_uses_workspace(tq, M, N, K):
         # batch and prefill sizes: transcode once per call into the workspace,
         # then the TQ2 kernels (both inside the timed call)
         ws = xs[("ws", N, K)]
@@ -168,7 +175,7 @@ def kernel_label(tq, fmt, M, N, K):
         return "tq2_bwd_x_kernel"
     if fmt == "ste":
         return "tq_ste_grad_w_kernel"
-    if fmt == "tq1" and M >= tq.tq_tq1_transcode_min_m(N, K):
+    if fmt == "tq1" and tq1_uses_workspace(tq, M, N, K):
         return "tq1_to_tq2_kernel + " + tq.tq_kernel_name(2, M, N, K)
     return tq.tq_kernel_name(2 if fmt == "tq2" else 1, M, N, K)
 
@@ -821,7 +828,13 @@ def main():
                     help="on-device ternarize + pack of a 28672 x 8192 latent matrix")
     ap.add_argument("--prefill", action="store_true",
                     help="prompt-sized products (M = 256 .. 4096) instead of the M <= 128 step")
+    ap.add_argument("--no-workspace", action="store_true",
+                    help="every TQ1 call through tq_gemm_tq1 (no workspace: the table-decode "
+                         "tiled kernel above 16 rows) instead of the workspace product from "
+                         "its switch point on")
     args = ap.parse_args()
+    global USE_WORKSPACE
+    USE_WORKSPACE = not args.no_workspace
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the product has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -939,6 +952,8 @@ def main():
         "dtype": "f16", "data": "synthetic",
         "config": {"workload": "TQ2 batch sweep M=1..128 and TQ1 M in {1,4,16,64} on "
                                "(K,N)=(8192,8192),(8192,28672); i.i.d. trits, fp16 block scales",
+                   "tq1_batch": "workspace product from its switch point" if USE_WORKSPACE
+                                else "no workspace (tq_gemm_tq1)",
                    "global_batch": None, "seq_len": None, "parallelism": "none"},
         "roofline": roofline_of(per_call),
     }
