@@ -46,10 +46,11 @@ TILES = [(mt, 4, ng, kg) for mt in (2, 4) for ng, kg in ((4, 2), (2, 4), (2, 2),
 TILES += [(mt, 2, ng, 4) for mt in (2, 4) for ng in (1, 2)]
 TILES.append((8, 2, 4, 2))
 TILES += [(2, 2, 1, 8), (2, 4, 1, 8)]
-# (M, N, K, ldq): K / 256 = 1, 3, 5, 7, 2 (every block trit offset 0..4 from
-# five blocks on; fewer blocks than k-groups); ldq above ceil(K / 5)
+# (M, N, K, ldq): K / 256 = 1, 3, 5, 7, 2, 112 (every block trit offset 0..4
+# from five blocks on; fewer blocks than k-groups; the down projection's
+# K = 28672, where byte offsets within a row pass 2^12); ldq above ceil(K / 5)
 TAB_SHAPES = [(17, 100, 256, None), (40, 300, 768, None), (64, 257, 1280, 272),
-              (100, 520, 1792, None), (130, 70, 512, 128)]
+              (100, 520, 1792, None), (130, 70, 512, 128), (33, 72, 28672, 5760)]
 
 
 @pytest.mark.parametrize("mt,nr,ng,kg", TILES)
