@@ -143,8 +143,8 @@ int tq_gemm_tq1(const void* X, const void* qs, int64_t ldq, const void* scales_f
                 int64_t M, int64_t N, int64_t K, void* stream);
 
 /* Name of the kernel that tq_gemm_tq2_ex (format = 2) or tq_gemm_tq1_ex
- * (format = 1) launches for this shape and path, as profilers show it, copied
- * NUL-terminated into name[cap].  TQ_ERR_SHAPE for an invalid shape,
+ * (format = 1, with ldq <= 2^22) launches for this shape and path, as
+ * profilers show it, copied NUL-terminated into name[cap].  TQ_ERR_SHAPE for an invalid shape,
  * TQ_ERR_VALUE for an unknown format or path, TQ_ERR_NULL for a NULL name,
  * TQ_ERR_UNSUPPORTED when the path is not available for the format.  Host
  * only; touches no device. */
