@@ -350,10 +350,11 @@ __device__ __forceinline__ void tiled_body(const uint16_t* __restrict__ X,
   using H0 = std::integral_constant<int, 0>;
   using H1 = std::integral_constant<int, 1>;
 
-  // Weights of round rd in B order and their scale pairs; a k-group without a
-  // block in the round (K / 256 not a multiple of KG) gets scale 0, so its
-  // block sum adds nothing and every wave runs the same straight-line code.
-  // T1: row group r of round rd's weights, decoded from the copied TQ1 bytes.
+  // Weights of round rd in B order and their scale pairs (read_w; read_w_row
+  // for one row group of 1.6-bit rows, decoded from the copied TQ1 bytes); a
+  // k-group without a block in the round (K / 256 not a multiple of KG) gets
+  // scale 0, so its block sum adds nothing and every wave runs the same
+  // straight-line code.
   auto read_w_row = [&](int rd, int r, u32x4* wbo, uint32_t* s2o) {
     const bool active = rd * KG + wk < nb;
     // Lane (li, g) wants weights 256 b + 64 g .. + 63 of its row: TQ1 bytes
@@ -391,11 +392,11 @@ __device__ __forceinline__ void tiled_body(const uint16_t* __restrict__ X,
     s2o[r] = active ? (sc | (sc << 16)) : 0u;
   };
   auto read_w = [&](int rd, u32x4* wbo, uint32_t* s2o) {
-    const bool active = rd * KG + wk < nb;
     if constexpr (T1) {
 #pragma unroll
       for (int r = 0; r < NR; ++r) read_w_row(rd, r, wbo, s2o);
     } else {
+      const bool active = rd * KG + wk < nb;
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
         wbo[r] = to_b_order(*reinterpret_cast<const u32x4*>(smem + wdst(rd) + w_rd + r * 1024));
