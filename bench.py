@@ -931,6 +931,8 @@ def main():
             "dtype": "f16", "data": "synthetic",
             "config": {"workload": "TQ2 and TQ1, M in {256, 1024, 4096} on (K,N)=(8192,8192),"
                                    "(8192,28672); i.i.d. trits, fp16 block scales",
+                       "tq1_batch": "workspace product from its switch point" if USE_WORKSPACE
+                                    else "no workspace (tq_gemm_tq1)",
                        "global_batch": None, "seq_len": None, "parallelism": "none"},
             "roofline": roofline_of(per_call),
             "tflops_total": round(sum(alg_flops(*c[1:]) for c in calls) / (ms_step * 1e-3) / 1e12,
