@@ -335,6 +335,48 @@ def context_bench(calls, per_call):
     return out
 
 
+def bwd_context(per_call, reps=3):
+    """Context beside the backward metric (not part of `value`): torch's dense
+    FP16 products (hipBLASLt) on the same shapes -- dX = dY W with an FP16
+    weight matrix, and dW = dY^T X with FP32 output (torch.mm out_dtype) --
+    timed with HIP events around `reps` back-to-back calls after two warm-up
+    calls, next to the library's kernels' own per-call times."""
+    import torch
+    out = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    for c in per_call:
+        M, N, K = c["M"], c["N"], c["K"]
+        dY = torch.randn(M, N, dtype=torch.float16, device="cuda")
+        if c["fmt"] == "bwd":
+            W = torch.randn(N, K, dtype=torch.float16, device="cuda")
+            fn = lambda: torch.mm(dY, W)  # noqa: E731
+            what = "dX = dY W, FP16 W"
+        else:
+            X = torch.randn(M, K, dtype=torch.float16, device="cuda")
+            try:
+                torch.mm(dY.t(), X, out_dtype=torch.float32)
+                fn = lambda: torch.mm(dY.t(), X, out_dtype=torch.float32)  # noqa: E731
+                what = "dW = dY^T X, FP32 out"
+            except (RuntimeError, TypeError):
+                fn = lambda: torch.mm(dY.t(), X)  # noqa: E731
+                what = "dW = dY^T X, FP16 out"
+        for _ in range(2):
+            fn()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        out.append({"fmt": c["fmt"], "M": M, "N": N, "K": K, "torch": what, "us": round(us, 1),
+                    "TFLOPps": round(alg_flops(M, N, K) / us / 1e6, 1),
+                    "ours_us": c["us"], "ours_over_torch_time": round(c["us"] / us, 3)})
+        del dY
+        torch.cuda.empty_cache()
+    return out
+
+
 def _time_graph(torch, launch, reps):
     """Average µs of one launch: a captured graph of ``reps`` calls of
     ``launch(i, stream)``, replayed once to warm up and once timed."""
@@ -909,6 +951,9 @@ def main():
             "tflops_total": round(sum(alg_flops(*c[1:]) for c in calls) / (ms_step * 1e-3) / 1e12,
                                   1),
         }
+        if not args.no_context:
+            log("[bench] context: torch dense FP16 products ...")
+            out["context"] = {"torch_dense_fp16": bwd_context(per_call)}
         if not args.no_cpu_baseline:
             log("[bench] CPU baseline (oracle) ...")
             cb = cpu_baseline(calls)
